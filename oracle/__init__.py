@@ -1,0 +1,169 @@
+"""Exact-value CPU oracle for the DSpark fused context-KV write.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+package never imports it, and it imports nothing from the product package.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, scalar loops); this
+module builds it with gcc, loads it with ctypes and wraps it for numpy
+arrays.  What it computes is stated, with its source on the vLLM API page
+"vllm.models.minimax_m3.common.ops.dspark_context_kv", in that file's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+HEAD_DIM = 128
+MAX_CAND = 4
+# Relative distance to a bf16 rounding midpoint within which both bf16
+# neighbours of the fp32 norm output are correct answers.  A 128-term fp32
+# sum, an rsqrt with <= 1 ulp error and three fp32 roundings stay below about
+# 2^-21 relative; 2^-18 leaves a factor-8 margin.
+NEAR_DELTA = 2.0 ** -18
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc and return its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+             "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.dspark_oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.dspark_oracle_bf16_decode.restype = ctypes.c_double
+        L.dspark_oracle_bf16_round.argtypes = [ctypes.c_double, ctypes.c_double,
+                                               ctypes.POINTER(ctypes.c_int),
+                                               ctypes.POINTER(ctypes.c_uint16)]
+        L.dspark_oracle_bf16_round.restype = ctypes.c_uint16
+        L.dspark_oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.dspark_oracle_e4m3_decode.restype = ctypes.c_double
+        L.dspark_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.dspark_oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.dspark_oracle_fp8_store.argtypes = [ctypes.c_uint16, ctypes.c_float]
+        L.dspark_oracle_fp8_store.restype = ctypes.c_uint8
+        L.dspark_oracle_ctx_kv_write.argtypes = [
+            P, i64, i32, i32,            # all_kv, num_ctx, L, nkv
+            P, ctypes.c_float,           # k_norm_weight, eps
+            P, P, i64, i32,              # positions, cos_sin, cs_rows, R
+            P, i64, i32,                 # slots, num_blocks, block_size
+            i32, P, P,                   # fp8, k_scales, v_scales
+            P,                           # caches (void**)
+            ctypes.c_double,             # near_delta
+            P, P, P, P, i64,             # alt_layer, alt_index, alt_count, alt_codes, cap
+            i64, i64]                    # t_begin, t_end
+        L.dspark_oracle_ctx_kv_write.restype = i64
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------- codecs ----
+
+def bf16_round(z: float, near_delta: float = 0.0):
+    """(code, near_tie, other_code) of the one-step bf16 RNE rounding of z."""
+    near = ctypes.c_int(0)
+    other = ctypes.c_uint16(0)
+    code = lib().dspark_oracle_bf16_round(float(z), float(near_delta),
+                                          ctypes.byref(near), ctypes.byref(other))
+    return int(code), bool(near.value), int(other.value)
+
+
+def bf16_decode(code: int) -> float:
+    return float(lib().dspark_oracle_bf16_decode(int(code) & 0xFFFF))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().dspark_oracle_e4m3_decode(int(code) & 0xFF))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().dspark_oracle_e4m3_encode(float(x)))
+
+
+def fp8_store(bf16_code: int, scale: float) -> int:
+    return int(lib().dspark_oracle_fp8_store(int(bf16_code) & 0xFFFF, float(scale)))
+
+
+# --------------------------------------------------------- the write ----
+
+@dataclass
+class OracleResult:
+    caches: list          # per-layer numpy arrays (uint16 or uint8), same shape as the device caches
+    alt_layer: np.ndarray  # int64 [n]
+    alt_index: np.ndarray  # int64 [n], element index into that layer's flat cache
+    alt_count: np.ndarray  # int32 [n]
+    alt_codes: np.ndarray  # uint16 [n, 4]
+
+
+def ctx_kv_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim,
+                 slot_mapping, caches, fp8, k_scales=None, v_scales=None,
+                 near_delta: float = NEAR_DELTA, t_begin: int = 0,
+                 t_end: int | None = None, alt_capacity: int | None = None) -> OracleResult:
+    """Run the oracle on host arrays.  ``caches`` (a list of per-layer numpy
+    arrays [num_blocks, nkv, bs, 256], uint16 for bf16 or uint8 for fp8) are
+    written in place and returned; every other input is read only.
+
+    all_kv: uint16 [num_ctx, L, 2, nkv, 128]; k_norm_weight: uint16 [L, 128];
+    positions, slot_mapping: int64 [num_ctx]; cos_sin: uint16 [rows, R];
+    k_scales, v_scales: float32 [L].
+    """
+    all_kv = np.ascontiguousarray(all_kv, dtype=np.uint16)
+    num_ctx, L, two, nkv, hd = all_kv.shape
+    assert two == 2 and hd == HEAD_DIM
+    w = np.ascontiguousarray(k_norm_weight, dtype=np.uint16)
+    assert w.shape == (L, HEAD_DIM)
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.uint16)
+    assert cs.ndim == 2 and cs.shape[1] == rotary_dim
+    assert len(caches) == L
+    want = np.uint8 if fp8 else np.uint16
+    for c in caches:
+        assert c.dtype == want and c.flags.c_contiguous and c.ndim == 4
+        assert c.shape == caches[0].shape and c.shape[1] == nkv and c.shape[3] == 2 * HEAD_DIM
+    num_blocks, _, bs, _ = caches[0].shape
+    ks = np.ascontiguousarray(k_scales if k_scales is not None else np.ones(L), dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales if v_scales is not None else np.ones(L), dtype=np.float32)
+    if t_end is None:
+        t_end = num_ctx
+    ptrs = (ctypes.c_void_p * L)(*[c.ctypes.data for c in caches])
+
+    cap = alt_capacity if alt_capacity is not None else max(1024, (t_end - t_begin) * L * nkv // 16)
+    while True:
+        a_layer = np.zeros(cap, np.int64)
+        a_index = np.zeros(cap, np.int64)
+        a_count = np.zeros(cap, np.int32)
+        a_codes = np.zeros((cap, MAX_CAND), np.uint16)
+        n = lib().dspark_oracle_ctx_kv_write(
+            all_kv.ctypes.data, num_ctx, L, nkv, w.ctypes.data, float(eps),
+            pos.ctypes.data, cs.ctypes.data, cs.shape[0], rotary_dim,
+            slots.ctypes.data, num_blocks, bs, 1 if fp8 else 0,
+            ks.ctypes.data, vs.ctypes.data, ctypes.cast(ptrs, ctypes.c_void_p),
+            float(near_delta), a_layer.ctypes.data, a_index.ctypes.data,
+            a_count.ctypes.data, a_codes.ctypes.data, cap, t_begin, t_end)
+        if n < 0:
+            raise ValueError("oracle precondition failed (code %d)" % n)
+        if n <= cap:
+            return OracleResult(caches, a_layer[:n], a_index[:n], a_count[:n], a_codes[:n])
+        cap = int(n)

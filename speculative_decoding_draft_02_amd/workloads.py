@@ -1,0 +1,249 @@
+"""Seeded synthetic inputs for the DSpark context-KV write.
+
+This module only draws inputs.  It holds none of the write's arithmetic, and
+both the device path (tests, bench) and the CPU oracle take their inputs from
+it.  Random normals come from numpy's PCG64 bits through an inverse-CDF table of
+normal quantiles rounded to bf16 by torch's CPU conversion (a library
+routine); the RoPE table is
+[cos(p * theta_i) | sin(p * theta_i)] with theta_i = 10000^(-2i/R), computed
+in fp64 and rounded to bf16 the same way.
+
+The five workloads follow the shapes of a MiniMax-M3.1 DSpark draft (L = 5
+draft layers, 128-dim heads, partial RoPE on 16/32/64 dims; the vLLM API page
+"vllm.models.minimax_m3.common.ops.dspark_context_kv") and the serving
+situations it is used in: a tiny case, a 4 x 1024-token prefill chunk with
+bf16 or fp8 caches, a 32768-token long context, and decode-step batches of
+1..8 accepted tokens per request.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+from scipy.special import ndtri
+
+HEAD_DIM = 128
+SENTINEL_BF16 = 0xFFFF   # a NaN pattern: never produced by the write
+SENTINEL_FP8 = 0xFF      # the e4m3 NaN pattern S.1111.111
+
+
+@dataclass
+class Workload:
+    name: str
+    num_ctx: int
+    num_layers: int
+    num_kv_heads: int
+    rotary_dim: int
+    block_size: int
+    num_blocks: int
+    fp8: bool
+    eps: float
+    all_kv: np.ndarray         # uint16 bf16 bits [num_ctx, L, 2, nkv, 128]
+    k_norm_weight: np.ndarray  # uint16 bf16 bits [L, 128]
+    positions: np.ndarray      # int64 [num_ctx]
+    slot_mapping: np.ndarray   # int64 [num_ctx], < 0 = padding
+    cos_sin: np.ndarray        # uint16 bf16 bits [rows, R] = [cos | sin]
+    k_scales: np.ndarray       # float32 [L]
+    v_scales: np.ndarray       # float32 [L]
+
+    @property
+    def sentinel(self) -> int:
+        return SENTINEL_FP8 if self.fp8 else SENTINEL_BF16
+
+    @property
+    def cache_shape(self):
+        return (self.num_blocks, self.num_kv_heads, self.block_size, 2 * HEAD_DIM)
+
+    @property
+    def cache_np_dtype(self):
+        return np.uint8 if self.fp8 else np.uint16
+
+    @property
+    def valid_tokens(self) -> int:
+        return int(np.count_nonzero(self.slot_mapping >= 0))
+
+    def new_host_caches(self):
+        return [np.full(self.cache_shape, self.sentinel, dtype=self.cache_np_dtype)
+                for _ in range(self.num_layers)]
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the write must move: all_kv rows of valid tokens read, cache
+        rows written, the cos/sin row and position of each valid token, every
+        slot, and the norm weights."""
+        v = self.valid_tokens
+        L, nkv, R = self.num_layers, self.num_kv_heads, self.rotary_dim
+        e = 1 if self.fp8 else 2
+        per_tok = L * 2 * nkv * HEAD_DIM * 2 + L * nkv * 2 * HEAD_DIM * e + 2 * R + 8
+        return v * per_tok + 8 * self.num_ctx + L * HEAD_DIM * 2
+
+    def token_layers(self) -> int:
+        return self.valid_tokens * self.num_layers
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32/fp64 array -> uint16 bf16 bits (round to nearest even), by torch."""
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def rope_table(rows: int, rotary_dim: int, theta: float = 10000.0) -> np.ndarray:
+    half = rotary_dim // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / rotary_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return to_bf16_bits(np.concatenate([np.cos(ang), np.sin(ang)], axis=1))
+
+
+_QBITS = 22
+_QTABLES = {}
+
+
+def _normal_table(std):
+    """bf16 bits of the N(0, std) quantiles at (i + 1/2) / 2^22, i < 2^22."""
+    tab = _QTABLES.get(std)
+    if tab is None:
+        u = (np.arange(1 << _QBITS, dtype=np.float64) + 0.5) / (1 << _QBITS)
+        tab = to_bf16_bits(ndtri(u) * std)
+        _QTABLES[std] = tab
+    return tab
+
+
+def _normal_bf16(rng, shape, std):
+    """N(0, std) samples as bf16 bits, by inverse CDF: 22 random bits pick one
+    of 2^22 equally likely quantiles (the tails beyond 5.17 std are cut).
+    Filled in chunks so that no large temporary is created."""
+    tab = _normal_table(float(std))
+    out = np.empty(shape, np.uint16)
+    flat = out.reshape(-1)
+    chunk = 1 << 20
+    for s in range(0, flat.size, chunk):
+        n = min(chunk, flat.size - s)
+        raw = rng.bit_generator.random_raw((n + 1) // 2)
+        idx = (raw.view(np.uint32)[:n] >> (32 - _QBITS))
+        np.take(tab, idx, out=flat[s:s + n])
+    return out
+
+
+def _pad(rng, slots, count):
+    if count:
+        idx = rng.choice(slots.size, size=count, replace=False)
+        slots[idx] = -1
+    return slots
+
+
+NAMES = ["tiny", "prefill_bf16", "prefill_fp8", "long_fp8", "decode_bf16"]
+
+DESCRIPTIONS = [
+    "num_ctx=64 L=1 nkv=2 R=64 bs=16 8 blocks bf16 cache, ~10% padding",
+    "num_ctx=4096 (4 x 1024) L=5 nkv=8 R=64 bs=64 512 blocks/layer bf16 caches, 2% padding",
+    "num_ctx=4096 (4 x 1024) L=5 nkv=8 R=64 bs=64 512 blocks/layer fp8 e4m3 caches, 2% padding",
+    "num_ctx=32768 (positions 8192..40959) L=5 nkv=8 R=32 bs=16 4096 blocks/layer fp8 e4m3 caches",
+    "decode: 64 requests x 1..8 tokens L=5 nkv=4 R=16 bs=128 512 blocks/layer bf16 caches, 25% padding",
+]
+
+
+def make(index: int, variant: int = 0) -> Workload:
+    """Workload ``index`` (0..4, in the order of NAMES).  ``variant`` > 0
+    draws an independent input set of the same shape (fresh values, slots
+    and positions) for benchmarks that rotate inputs."""
+    seed = 1000 + index + 7919 * variant
+    rng = np.random.default_rng(seed)
+    eps = 1e-6
+    if index == 0:
+        N, L, nkv, R, bs, nb, fp8 = 64, 1, 2, 64, 16, 8, False
+        all_kv = _normal_bf16(rng, (N, L, 2, nkv, HEAD_DIM), 1.0)
+        w = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+        slots = rng.permutation(nb * bs)[:N].astype(np.int64)
+        slots = _pad(rng, slots, int(round(0.10 * N)))
+        positions = np.arange(N, dtype=np.int64)
+        cs = rope_table(4096, R)
+    elif index in (1, 2):
+        fp8 = index == 2
+        reqs, per = 4, 1024
+        N, L, nkv, R, bs, nb = reqs * per, 5, 8, 64, 64, 512
+        all_kv = _normal_bf16(rng, (N, L, 2, nkv, HEAD_DIM), 4.0 if fp8 else 1.0)
+        w = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+        if fp8:
+            ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+            vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        else:
+            ks = np.ones(L, np.float32)
+            vs = np.ones(L, np.float32)
+        bpr = per // bs
+        blocks = rng.permutation(nb)[:reqs * bpr].reshape(reqs, bpr)
+        j = np.arange(per, dtype=np.int64)
+        slots = np.concatenate([blocks[r][j // bs] * bs + j % bs for r in range(reqs)]).astype(np.int64)
+        slots = _pad(rng, slots, int(round(0.02 * N)))
+        positions = np.tile(np.arange(per, dtype=np.int64), reqs)
+        cs = rope_table(4096, R)
+        if fp8:
+            # Deterministic saturation probes in V: +-(448 * v_scale) times
+            # {0.999, 1, 464/448, 1.2, 3}, at the first valid token, head 0.
+            t0 = int(np.flatnonzero(slots >= 0)[0])
+            mult = np.array([0.999, 1.0, 464.0 / 448.0, 1.2, 3.0])
+            for l in range(L):
+                vals = np.concatenate([mult, -mult]) * 448.0 * float(vs[l])
+                all_kv[t0, l, 1, 0, :vals.size] = to_bf16_bits(vals.astype(np.float32))
+    elif index == 3:
+        N, L, nkv, R, bs, nb, fp8 = 32768, 5, 8, 32, 16, 4096, True
+        all_kv = _normal_bf16(rng, (N, L, 2, nkv, HEAD_DIM), 1.0)
+        w = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+        ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        perm = rng.permutation(nb).astype(np.int64)
+        positions = np.arange(8192, 8192 + N, dtype=np.int64)
+        slots = perm[positions // bs] * bs + positions % bs
+        cs = rope_table(65536, R)
+    elif index == 4:
+        L, nkv, R, bs, nb, fp8 = 5, 4, 16, 128, 512, False
+        reqs = 64
+        n_i = rng.integers(1, 9, size=reqs)
+        N = int(n_i.sum())
+        all_kv = _normal_bf16(rng, (N, L, 2, nkv, HEAD_DIM), 1.0)
+        w = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+        p0 = rng.integers(0, 131072 - 8 + 1, size=reqs)
+        free_blocks = list(rng.permutation(nb))
+        pos_list, slot_list = [], []
+        for r in range(reqs):
+            p = np.arange(p0[r], p0[r] + n_i[r], dtype=np.int64)
+            logical = p // bs
+            first = int(logical[0])
+            table = [int(free_blocks.pop()) for _ in range(int(logical[-1]) - first + 1)]
+            slot_list.append(np.array([table[int(lb) - first] for lb in logical], np.int64) * bs + p % bs)
+            pos_list.append(p)
+        positions = np.concatenate(pos_list)
+        slots = _pad(rng, np.concatenate(slot_list), int(round(0.25 * N)))
+        cs = rope_table(131072, R)
+    else:
+        raise ValueError("workload index must be 0..4")
+    return Workload(NAMES[index], N, L, nkv, R, bs, nb, fp8, eps,
+                    np.ascontiguousarray(all_kv), np.ascontiguousarray(w),
+                    positions, slots, cs, ks, vs)
+
+
+def custom(num_ctx, num_layers, num_kv_heads, rotary_dim, block_size, num_blocks,
+           fp8, seed, pad_fraction=0.1, kv_std=1.0, w_std=0.1, cs_rows=None,
+           eps=1e-6) -> Workload:
+    """A small workload of arbitrary shape with unique random slots."""
+    rng = np.random.default_rng(seed)
+    N, L, nkv = num_ctx, num_layers, num_kv_heads
+    assert N <= num_blocks * block_size
+    all_kv = _normal_bf16(rng, (N, L, 2, nkv, HEAD_DIM), kv_std)
+    w = _normal_bf16(rng, (L, HEAD_DIM), w_std)
+    if fp8:
+        ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+    else:
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+    slots = rng.permutation(num_blocks * block_size)[:N].astype(np.int64)
+    slots = _pad(rng, slots, int(round(pad_fraction * N)))
+    rows = cs_rows if cs_rows is not None else max(N, 1) + 64
+    positions = rng.integers(0, rows, size=N).astype(np.int64)
+    cs = rope_table(rows, rotary_dim)
+    return Workload("custom", N, L, nkv, rotary_dim, block_size, num_blocks, fp8, eps,
+                    all_kv, w, positions, slots, cs, ks, vs)

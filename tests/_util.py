@@ -1,0 +1,117 @@
+"""Shared helpers for the tests: row specs, single-row runs of the oracle and
+an independent PyTorch CPU version of the unfused chain."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from speculative_decoding_draft_02_amd import workloads as W
+
+HEAD_DIM = 128
+
+
+def bf16_bits(values) -> np.ndarray:
+    return W.to_bf16_bits(np.asarray(values, dtype=np.float64))
+
+
+def bits_to_f32(codes: np.ndarray) -> np.ndarray:
+    return (np.asarray(codes, dtype=np.uint32) << 16).view(np.float32)
+
+
+def row_from_spec(spec, n=HEAD_DIM, dtype=float):
+    row = np.full(n, spec.get("all", 0), dtype=dtype)
+    for k, v in (spec.get("at") or {}).items():
+        row[int(k)] = v
+    return row
+
+
+def run_oracle_rows(oracle, k_rows, v_rows, w_rows, positions, rotary_dim, cos_sin=None,
+                    eps=1e-6, fp8=False, k_scale=1.0, v_scale=1.0, block_size=1,
+                    slots=None, num_blocks=None):
+    """Write N tokens of one layer and one head, token t at slot t (or
+    ``slots``), and return (K codes [N,128], V codes [N,128], result)."""
+    k_rows = np.atleast_2d(np.asarray(k_rows, dtype=np.uint16))
+    v_rows = np.atleast_2d(np.asarray(v_rows, dtype=np.uint16))
+    N = k_rows.shape[0]
+    all_kv = np.stack([k_rows, v_rows], axis=1)[:, None, :, None, :]  # [N,1,2,1,128]
+    w = np.asarray(w_rows, dtype=np.uint16).reshape(1, HEAD_DIM)
+    pos = np.asarray(positions, dtype=np.int64).reshape(N)
+    if cos_sin is None:
+        cos_sin = W.rope_table(int(pos.max()) + 1, rotary_dim)
+    slots = np.arange(N, dtype=np.int64) if slots is None else np.asarray(slots, np.int64)
+    nb = num_blocks if num_blocks is not None else (N + block_size - 1) // block_size
+    dt = np.uint8 if fp8 else np.uint16
+    cache = np.full((nb, 1, block_size, 256), 0xFF if fp8 else 0xFFFF, dtype=dt)
+    res = oracle.ctx_kv_write(all_kv, w, eps, pos, cos_sin, rotary_dim, slots, [cache],
+                              fp8, np.array([k_scale], np.float32),
+                              np.array([v_scale], np.float32))
+    rows = cache.reshape(-1, 256)
+    sel = slots[slots >= 0]
+    return rows[sel, :128], rows[sel, 128:], res
+
+
+def compact_blocks(wl: W.Workload) -> W.Workload:
+    """The same workload with its used cache blocks renumbered 0..n-1, so the
+    host caches hold only blocks that some slot touches (same values, same
+    in-block offsets; keeps CPU-side tests small)."""
+    import dataclasses
+    s = wl.slot_mapping
+    blocks = np.unique(s[s >= 0] // wl.block_size)
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    new = np.array([remap[int(x) // wl.block_size] * wl.block_size + int(x) % wl.block_size
+                    if x >= 0 else -1 for x in s], np.int64)
+    return dataclasses.replace(wl, slot_mapping=new, num_blocks=max(len(blocks), 1))
+
+
+# ------------------------------------------------------------------------
+# The unfused chain on the CPU with PyTorch library ops in fp32, written from
+# the list of steps the fused write replaces (vLLM API page
+# "vllm.models.minimax_m3.common.ops.dspark_context_kv", module docstring):
+# permute copy, per-layer K norm + stack, positions.repeat, rotary_embedding
+# (NeoX), per-layer reshape_and_cache_flash.  It is an independent second
+# implementation used to cross-check the oracle, not the oracle itself.
+
+def torch_unfused(wl: W.Workload):
+    kv = torch.from_numpy(wl.all_kv.view(np.int16)).view(torch.bfloat16)  # [N,L,2,H,D]
+    N, L, _, H, D = kv.shape
+    R = wl.rotary_dim
+    all_k = kv[:, :, 0].permute(1, 0, 2, 3).contiguous()          # [L,N,H,D]
+    all_v = kv[:, :, 1].permute(1, 0, 2, 3).contiguous()
+    w = torch.from_numpy(wl.k_norm_weight.view(np.int16)).view(torch.bfloat16).float()
+    normed = []
+    for l in range(L):
+        x = all_k[l].float()
+        var = x.pow(2).mean(dim=-1, keepdim=True)
+        normed.append((x * torch.rsqrt(var + wl.eps) * (1.0 + w[l])).to(torch.bfloat16))
+    k = torch.stack(normed)                                        # [L,N,H,D]
+    pos = torch.from_numpy(wl.positions).repeat(L)                 # [L*N]
+    cs = torch.from_numpy(wl.cos_sin.view(np.int16)).view(torch.bfloat16)
+    cos = cs[pos, : R // 2].float().view(L, N, 1, R // 2)
+    sin = cs[pos, R // 2:].float().view(L, N, 1, R // 2)
+    x1 = k[..., : R // 2].float()
+    x2 = k[..., R // 2: R].float()
+    o1 = (x1 * cos - x2 * sin).to(torch.bfloat16)
+    o2 = (x2 * cos + x1 * sin).to(torch.bfloat16)
+    k = torch.cat([o1, o2, k[..., R:]], dim=-1)
+    caches = wl.new_host_caches()
+    slots = torch.from_numpy(wl.slot_mapping)
+    valid = torch.nonzero(slots >= 0).flatten()
+    s = slots[valid]
+    blk, off = s // wl.block_size, s % wl.block_size
+    for l in range(L):
+        kk, vv = k[l, valid], all_v[l, valid]                      # [V,H,D]
+        if wl.fp8:
+            kq = (kk.float() / float(wl.k_scales[l])).clamp(-448.0, 448.0)
+            vq = (vv.float() / float(wl.v_scales[l])).clamp(-448.0, 448.0)
+            kb = kq.to(torch.float8_e4m3fn).view(torch.uint8)
+            vb = vq.to(torch.float8_e4m3fn).view(torch.uint8)
+            flat = torch.from_numpy(caches[l].reshape(-1, 256))
+        else:
+            kb = kk.view(torch.int16)
+            vb = vv.view(torch.int16)
+            flat = torch.from_numpy(caches[l].view(np.int16).reshape(-1, 256))
+        for h in range(H):
+            rows = (blk * H + h) * wl.block_size + off
+            flat[rows, :128] = kb[:, h]
+            flat[rows, 128:] = vb[:, h]
+    return caches

@@ -1,0 +1,321 @@
+"""Pins of the oracle's context-KV write against closed forms, invariants
+that the definition fixes, exact rational arithmetic, and an independent
+PyTorch CPU implementation of the unfused chain.
+
+Definition: vLLM API page "vllm.models.minimax_m3.common.ops.dspark_context_kv"
+(module docstring; DSparkContextKVWriter; rotary_dims_supported)."""
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import yaml
+
+from oracle import compare as C
+from speculative_decoding_draft_02_amd import workloads as W
+
+from _util import (bf16_bits, bits_to_f32, compact_blocks, row_from_spec, run_oracle_rows,
+                   torch_unfused)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "norm_rope_closed_forms.yaml")) as f:
+        return yaml.safe_load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["cases"], ids=lambda c: c["name"])
+def test_closed_forms_bf16(oracle_lib, case):
+    x = bf16_bits(row_from_spec(case["x"]))
+    w = bf16_bits(row_from_spec(case["w"]))
+    v = bf16_bits(np.linspace(-2, 2, 128))
+    k, vout, _ = run_oracle_rows(oracle_lib, x, v, w, [case["position"]], case["rotary_dim"],
+                                 eps=case.get("eps", 1e-6))
+    want = row_from_spec(case["expect_k"], dtype=np.int64).astype(np.uint16)
+    assert np.array_equal(k[0], want), (case["name"], [hex(a) for a in k[0][:8]])
+    assert np.array_equal(vout[0], v)
+
+
+@pytest.mark.parametrize("case", _golden()["fp8_cases"], ids=lambda c: c["name"])
+def test_closed_forms_fp8(oracle_lib, case):
+    x = bf16_bits(row_from_spec(case["x"]))
+    w = bf16_bits(row_from_spec(case["w"]))
+    v = bf16_bits(np.zeros(128))
+    k, _, _ = run_oracle_rows(oracle_lib, x, v, w, [case["position"]], case["rotary_dim"],
+                              fp8=True, k_scale=case["k_scale"], v_scale=1.0)
+    want = row_from_spec(case["expect_k"], dtype=np.int64).astype(np.uint8)
+    assert np.array_equal(k[0], want), case["name"]
+
+
+def _rand_rows(seed, n, std=1.0):
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal((n, 128)) * std)
+
+
+def test_norm_sign_symmetry(oracle_lib):
+    x = _rand_rows(1, 6)
+    w = bf16_bits(np.random.default_rng(2).standard_normal(128) * 0.1)
+    v = _rand_rows(3, 6)
+    k1, _, _ = run_oracle_rows(oracle_lib, x, v, w, np.arange(6) * 37, 64)
+    k2, _, _ = run_oracle_rows(oracle_lib, x ^ 0x8000, v, w, np.arange(6) * 37, 64)
+    assert np.array_equal(k1 ^ 0x8000, k2)
+
+
+def test_w_minus_one_gives_signed_zeros(oracle_lib):
+    x = _rand_rows(4, 3)
+    w = bf16_bits(np.full(128, -1.0))
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, [0, 0, 0], 64)
+    # norm output is +-0 with the sign of x; dims past R pass it through,
+    # the rotated dims are zeros whose sign follows the RoPE arithmetic
+    assert np.array_equal(k[:, 64:], x[:, 64:] & 0x8000)
+    assert np.all((k[:, :64] & 0x7FFF) == 0)
+
+
+def _norm_only(oracle_lib, x, w, eps=1e-6):
+    """Norm output through the write at position 0 (cos = 1, sin = 0)."""
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, np.zeros(len(x), np.int64), 16, eps=eps)
+    return k
+
+
+@pytest.mark.parametrize("R", [16, 32, 64])
+def test_pass_through_dims_equal_norm_output(oracle_lib, R):
+    x = _rand_rows(5, 8)
+    w = bf16_bits(np.random.default_rng(6).standard_normal(128) * 0.1)
+    y = _norm_only(oracle_lib, x, w)
+    pos = np.arange(8) * 101 + 3
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, pos, R)
+    assert np.array_equal(k[:, R:], y[:, R:])
+    assert not np.array_equal(k[:, :R], y[:, :R])
+
+
+def _crafted_table(R, cos, sin):
+    return bf16_bits(np.concatenate([np.full(R // 2, cos), np.full(R // 2, sin)])[None, :])
+
+
+@pytest.mark.parametrize("R", [16, 32, 64])
+def test_rope_quarter_turn_and_half_turn(oracle_lib, R):
+    """cos = 0, sin = 1 maps (a, b) -> (-b, a); cos = -1, sin = 0 negates:
+    both exact, so the rotated codes are sign flips and swaps of y."""
+    x = _rand_rows(8, 4)
+    w = bf16_bits(np.random.default_rng(9).standard_normal(128) * 0.1)
+    y = _norm_only(oracle_lib, x, w)
+    h = R // 2
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, [0] * 4, R, cos_sin=_crafted_table(R, 0.0, 1.0))
+    assert np.array_equal(k[:, :h], y[:, h:R] ^ 0x8000)
+    assert np.array_equal(k[:, h:R], y[:, :h])
+    assert np.array_equal(k[:, R:], y[:, R:])
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, [0] * 4, R, cos_sin=_crafted_table(R, -1.0, 0.0))
+    assert np.array_equal(k[:, :R], y[:, :R] ^ 0x8000)
+
+
+def test_rope_uses_the_tokens_row_and_neox_pairs(oracle_lib):
+    """Row p of the table rotates pair (i, i + R/2) by its own (cos, sin);
+    the result matches the exact product, rounded once, for every element."""
+    R = 32
+    x = _rand_rows(10, 5)
+    w = bf16_bits(np.zeros(128))
+    y = bits_to_f32(_norm_only(oracle_lib, x, w)).astype(np.float64)
+    table = W.rope_table(2000, R)
+    pos = np.array([0, 1, 17, 999, 1999])
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, pos, R, cos_sin=table)
+    cs = bits_to_f32(table[pos]).astype(np.float64)
+    c, s = cs[:, : R // 2], cs[:, R // 2:]
+    a, b = y[:, : R // 2], y[:, R // 2: R]
+    first = (a * c - b * s)
+    second = (b * c + a * s)
+    # fp64 products of bf16 values are exact: the stored value must be
+    # within half a bf16 ulp (2^(floor(log2|v|) - 7)) of the exact result
+    got = bits_to_f32(k[:, :R]).astype(np.float64)
+    want = np.concatenate([first, second], axis=1)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+    assert np.all(np.abs(got - want) <= ulp / 2)
+
+
+def test_rope_norm_preservation(oracle_lib):
+    """(ac - bs)^2 + (bc + as)^2 = (a^2 + b^2)(c^2 + s^2): holds for the
+    stored pair within the two bf16 roundings."""
+    R = 64
+    x = _rand_rows(12, 16)
+    w = bf16_bits(np.random.default_rng(13).standard_normal(128) * 0.1)
+    y = bits_to_f32(_norm_only(oracle_lib, x, w)).astype(np.float64)
+    table = W.rope_table(4096, R)
+    pos = np.random.default_rng(14).integers(0, 4096, 16)
+    k, _, _ = run_oracle_rows(oracle_lib, x, x, w, pos, R, cos_sin=table)
+    kf = bits_to_f32(k).astype(np.float64)
+    cs = bits_to_f32(table[pos]).astype(np.float64)
+    c, s = cs[:, :R // 2], cs[:, R // 2:]
+    lhs = kf[:, :R // 2] ** 2 + kf[:, R // 2:R] ** 2
+    rhs = (y[:, :R // 2] ** 2 + y[:, R // 2:R] ** 2) * (c ** 2 + s ** 2)
+    mag = np.sqrt(rhs) + 1e-30
+    # each stored value is within 2^-9 relative of the exact one
+    assert np.all(np.abs(np.sqrt(lhs) - np.sqrt(rhs)) <= mag * 2.0 ** -8)
+
+
+def test_norm_rounding_matches_exact_rationals(oracle_lib):
+    """Brute force in exact arithmetic: z_i = x_i (1 + w_i) / sqrt(sum x^2/128 + eps)
+    with rationals (sqrt to 60 digits), rounded once to bf16 by comparing
+    with the two neighbouring bf16 values."""
+    getcontext().prec = 60
+    x = _rand_rows(20, 4)
+    w = bf16_bits(np.random.default_rng(21).standard_normal(128) * 0.1)
+    y = _norm_only(oracle_lib, x, w)
+    eps = Fraction(float(np.float32(1e-6)))
+    xf = bits_to_f32(x)
+    wf = bits_to_f32(w)
+    for r in range(4):
+        ss = sum(Fraction(float(v)) ** 2 for v in xf[r])
+        m = ss / 128 + eps
+        root = Decimal(m.numerator) / Decimal(m.denominator)
+        inv = Fraction(1) / Fraction(root.sqrt())
+        for i in range(0, 128, 7):
+            z = Fraction(float(xf[r, i])) * inv * (1 + Fraction(float(wf[i])))
+            got = Fraction(float(bits_to_f32(np.array([y[r, i]]))[0]))
+            # the chosen bf16 value is nearest: no bf16 neighbour is closer
+            code = int(y[r, i])
+            for nb in (code - 1, code + 1):
+                if (nb & 0x7FFF) in (0x7F80,) or nb < 0 or nb > 0xFFFF:
+                    continue
+                alt = Fraction(float(bits_to_f32(np.array([nb]))[0]))
+                assert abs(z - got) <= abs(z - alt), (r, i)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_v_is_stored_as_defined(oracle_lib, fp8):
+    x = _rand_rows(30, 8)
+    v = _rand_rows(31, 8, std=3.0)
+    w = bf16_bits(np.zeros(128))
+    vs = 0.07
+    _, vout, _ = run_oracle_rows(oracle_lib, x, v, w, np.arange(8), 64, fp8=fp8, v_scale=vs)
+    if not fp8:
+        assert np.array_equal(vout, v)       # a bit copy
+        return
+    import oracle
+    dec = np.vectorize(oracle.e4m3_decode)(vout.astype(np.int64))
+    vf = bits_to_f32(v).astype(np.float64) / np.float32(vs)
+    sat = np.abs(vf) >= 448
+    assert np.all(np.abs(dec[sat]) == 448)
+    # within half an e4m3 step of the quotient
+    step = np.where(np.abs(vf) < 2 ** -6, 2.0 ** -9,
+                    2.0 ** (np.floor(np.log2(np.maximum(np.abs(vf), 1e-30))) - 3))
+    assert np.all(np.abs(dec[~sat] - vf[~sat]) <= step[~sat] / 2 * (1 + 1e-6))
+
+
+def test_padding_and_placement(oracle_lib):
+    """Token t lands at cache[slot // bs, h, slot % bs]; padded tokens and
+    every other row keep their previous bytes."""
+    wl = W.custom(num_ctx=12, num_layers=2, num_kv_heads=3, rotary_dim=32, block_size=4,
+                  num_blocks=5, fp8=False, seed=3, pad_fraction=0.25)
+    caches = wl.new_host_caches()
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  wl.rotary_dim, wl.slot_mapping, caches, False)
+    written = 0
+    for t, s in enumerate(wl.slot_mapping):
+        if s < 0:
+            continue
+        for l in range(2):
+            for h in range(3):
+                row = caches[l][s // 4, h, s % 4]
+                assert np.array_equal(row[128:], wl.all_kv[t, l, 1, h])
+                assert not np.any(row[:128] == 0xFFFF)
+                written += 1
+    total_rows = sum(c.reshape(-1, 256).shape[0] for c in caches)
+    untouched = sum(int(np.count_nonzero(np.all(c.reshape(-1, 256) == 0xFFFF, axis=1)))
+                    for c in caches)
+    assert untouched == total_rows - written
+    assert written == 2 * 3 * int(np.count_nonzero(wl.slot_mapping >= 0))
+
+
+def test_layers_use_their_own_weights_and_scales(oracle_lib):
+    wl = W.custom(num_ctx=6, num_layers=3, num_kv_heads=1, rotary_dim=16, block_size=2,
+                  num_blocks=4, fp8=True, seed=8, pad_fraction=0.0)
+    # same K and V in every layer: outputs must differ only through w and scales
+    wl.all_kv[:, 1:] = wl.all_kv[:, :1]
+    wl.k_scales[:] = np.float32([0.1, 0.2, 0.4])
+    wl.v_scales[:] = np.float32([0.4, 0.2, 0.1])
+    wl.k_norm_weight[:] = wl.k_norm_weight[0]
+    caches = wl.new_host_caches()
+    oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                            16, wl.slot_mapping, caches, True, wl.k_scales, wl.v_scales)
+    import oracle
+    dec = np.vectorize(oracle.e4m3_decode)
+    k = [dec(c[..., :128].astype(np.int64)) * s for c, s in zip(caches, wl.k_scales)]
+    v = [dec(c[..., 128:].astype(np.int64)) * s for c, s in zip(caches, wl.v_scales)]
+    written = caches[0][..., 0] != 0xFF
+    for l in (1, 2):
+        # dequantised values agree within the coarser layer's e4m3 step
+        assert np.allclose(k[l][written], k[0][written], rtol=0.13, atol=0.05)
+        assert np.allclose(v[l][written], v[0][written], rtol=0.13, atol=0.1)
+    assert not np.array_equal(caches[1], caches[0])
+
+
+# ------------------------------------------------- independent cross-check --
+
+SWEEP = [
+    # (N, L, nkv, R, bs, blocks, fp8, pad)
+    (1, 1, 1, 16, 1, 2, False, 0.0),
+    (3, 2, 1, 32, 2, 3, True, 0.34),
+    (4, 1, 2, 64, 16, 1, False, 0.25),
+    (4, 2, 2, 16, 16, 1, True, 0.0),
+    (4, 2, 2, 64, 1, 8, True, 0.5),
+    (4, 1, 1, 32, 2, 4, False, 1.0),      # every slot is padding
+    (2, 2, 2, 32, 16, 2, False, 0.0),
+    (37, 3, 3, 64, 8, 7, True, 0.1),
+    (50, 2, 4, 16, 4, 16, False, 0.2),
+]
+
+
+@pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "N%d-L%d-H%d-R%d-bs%d-%s" % (s[0], s[1], s[2], s[3], s[4], "fp8" if s[6] else "bf16"))
+def test_oracle_vs_torch_unfused(oracle_lib, shape):
+    N, L, nkv, R, bs, nb, fp8, pad = shape
+    wl = W.custom(N, L, nkv, R, bs, nb, fp8, seed=hash(shape) % 1000, pad_fraction=pad,
+                  kv_std=4.0 if fp8 else 1.0)
+    ref = torch_unfused(wl)
+    caches = wl.new_host_caches()
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  R, wl.slot_mapping, caches, fp8, wl.k_scales, wl.v_scales)
+    rep = C.compare(ref, res, wl.slot_mapping, fp8, wl.sentinel)
+    assert rep.failures == 0, rep.summary()
+
+
+@pytest.mark.parametrize("index", [0, 4])
+def test_oracle_vs_torch_unfused_workloads(oracle_lib, index):
+    wl = compact_blocks(W.make(index))
+    ref = torch_unfused(wl)
+    caches = wl.new_host_caches()
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  wl.rotary_dim, wl.slot_mapping, caches, wl.fp8,
+                                  wl.k_scales, wl.v_scales)
+    rep = C.compare(ref, res, wl.slot_mapping, wl.fp8, wl.sentinel)
+    tot = rep.totals()
+    assert rep.failures == 0, tot
+    # the fp32 chain and the exact oracle agree almost everywhere
+    assert tot["k"]["exact"] >= 0.99 * tot["k"]["n"]
+
+
+def test_acceptance_rule_catches_planted_mistakes(oracle_lib):
+    """Mistakes planted in an oracle-side result (not the device path) must
+    be reported: a sign flip, a 2-ulp error, a V bit change, a stray write."""
+    wl = W.custom(8, 2, 2, 32, 4, 6, False, seed=4, pad_fraction=0.25)
+    caches = wl.new_host_caches()
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  32, wl.slot_mapping, caches, False)
+    good = [c.copy() for c in caches]
+    assert C.compare(good, res, wl.slot_mapping, False, wl.sentinel).failures == 0
+    t = int(np.flatnonzero(wl.slot_mapping >= 0)[0])
+    s = int(wl.slot_mapping[t])
+    for mutate in ("sign", "two_ulp", "v_bit", "stray"):
+        bad = [c.copy() for c in good]
+        row = bad[1][s // 4, 1, s % 4]
+        if mutate == "sign":
+            row[3] ^= 0x8000
+            if row[3] in (0x0000, 0x8000):
+                row[3] = 0x4000
+        elif mutate == "two_ulp":
+            row[40] = row[40] + 2
+        elif mutate == "v_bit":
+            row[130] ^= 1
+        else:
+            bad[0][5, 0, 3, 7] = 0
+        assert C.compare(bad, res, wl.slot_mapping, False, wl.sentinel).failures > 0, mutate
