@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused DSpark context-KV write on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one write (norm + RoPE + store of every layer's context K/V) over
+one batch of synthetic input already resident in HBM.  The headline line is
+the 4 x 1024-token prefill chunk with bf16 caches (L = 5 draft layers, 8 kv
+heads, 128-dim heads, rotary dim 64); the fp8, long-context and decode
+workloads are measured in the same run and reported under "workloads".
+
+Throughput is algorithmic bytes / time: all_kv rows read for valid tokens,
+cache rows written, the cos/sin row and position of each valid token, every
+slot, and the norm weights.  Inputs rotate over several independently drawn
+sets so that one cycle's footprint exceeds the 256 MB last-level cache and
+the figure is HBM bandwidth, not cache bandwidth.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from speculative_decoding_draft_02_amd import _lib  # noqa: E402
+from speculative_decoding_draft_02_amd import workloads as W  # noqa: E402
+from speculative_decoding_draft_02_amd.writer import AttnLayer, DSparkContextKVWriter  # noqa: E402
+
+METRIC = "context-KV write HBM GB/s (% of MI355X peak) and token-layers/s"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["speculative_decoding_draft_02_amd/csrc/ctx_kv_kernel.hip",
+                  "speculative_decoding_draft_02_amd/csrc/ctx_kv_writer.cpp",
+                  "speculative_decoding_draft_02_amd/csrc/ctx_kv_args.h"]
+HEADLINE = 1   # index of the prefill bf16 workload
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bf16_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+class Setup:
+    """Caches + writer for a workload shape, and `n_sets` input sets."""
+
+    def __init__(self, index: int, n_sets: int, dev):
+        self.index = index
+        self.sets = [W.make(index, variant=v) for v in range(n_sets)]
+        wl = self.sets[0]
+        self.wl = wl
+        layers = []
+        for l in range(wl.num_layers):
+            if wl.fp8:
+                cache = torch.full(wl.cache_shape, 0xFF, dtype=torch.uint8, device=dev)
+            else:
+                cache = torch.full(wl.cache_shape, -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+            ks = torch.tensor([float(wl.k_scales[l])], dtype=torch.float32, device=dev)
+            vs = torch.tensor([float(wl.v_scales[l])], dtype=torch.float32, device=dev)
+            layers.append(AttnLayer(cache, ks, vs, "fp8" if wl.fp8 else "auto"))
+        self.layers = layers
+        self.writer = DSparkContextKVWriter(layers)
+        self.inputs = []
+        for s in self.sets:
+            self.inputs.append(dict(
+                all_kv=bf16_dev(s.all_kv, dev), w=bf16_dev(s.k_norm_weight, dev),
+                positions=torch.from_numpy(s.positions).to(dev),
+                cos_sin=bf16_dev(s.cos_sin, dev),
+                slots=torch.from_numpy(s.slot_mapping).to(dev)))
+        # one checked call through the Python writer builds the tables
+        i0 = self.inputs[0]
+        self.writer(i0["all_kv"], i0["w"], wl.eps, i0["positions"], i0["cos_sin"],
+                    wl.rotary_dim, i0["slots"])
+        torch.cuda.synchronize()
+        self.handle = self.writer._handle
+        self.bytes = [s.algorithmic_bytes() for s in self.sets]
+        self.token_layers = [s.token_layers() for s in self.sets]
+
+    def launch(self, k: int, stream_ptr) -> None:
+        """One write of input set k % n through the C ABI (arguments already
+        checked by the Python writer on the same tensors)."""
+        i = self.inputs[k % len(self.inputs)]
+        wl = self.wl
+        st = _lib.dspark_ctx_kv_writer_write(
+            self.handle, i["all_kv"].data_ptr(), wl.num_ctx, wl.num_layers, wl.num_kv_heads,
+            i["w"].data_ptr(), wl.eps, i["positions"].data_ptr(), i["cos_sin"].data_ptr(),
+            i["cos_sin"].shape[0], wl.rotary_dim, i["slots"].data_ptr(), stream_ptr)
+        if st != _lib.OK:
+            raise RuntimeError(_lib.dspark_ctx_kv_last_error())
+
+
+def time_eager(setup: Setup, steps: int, warmup: int, stream):
+    """Warm up, then time exactly `steps` launches: one event pair around
+    each launch (kernel duration) and the whole region (per-step time)."""
+    sp = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for k in range(warmup):
+            setup.launch(k, sp)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            starts[k].record(stream)
+            setup.launch(warmup + k, sp)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3   # seconds
+    region = starts[0].elapsed_time(ends[-1]) * 1e-3
+    nbytes = np.array([setup.bytes[(warmup + k) % len(setup.bytes)] for k in range(steps)])
+    ntl = np.array([setup.token_layers[(warmup + k) % len(setup.bytes)] for k in range(steps)])
+    return dict(region_s=region, wall_s=wall, kernel_s=per, bytes=nbytes, token_layers=ntl)
+
+
+def time_graph(setup: Setup, steps: int, warmup: int, stream):
+    """Capture one write in a HIP graph and replay it `steps` times."""
+    sp = stream.cuda_stream
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            setup.launch(0, torch.cuda.current_stream().cuda_stream)
+        for _ in range(warmup):
+            g.replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+    region = start.elapsed_time(end) * 1e-3
+    del g
+    return dict(region_s=region, per_call_s=region / steps, bytes=setup.bytes[0],
+                token_layers=setup.token_layers[0])
+
+
+def cpu_baseline(index: int, budget_s: float = 12.0):
+    """The oracle, single-threaded on this host, on a bounded token sample of
+    the workload (test infrastructure: only this leg of the bench uses it)."""
+    sys.path.insert(0, ROOT)
+    import oracle
+    oracle.build()
+    wl = W.make(index)
+    caches = wl.new_host_caches()
+
+    def run(t_end, t_begin=0):
+        t0 = time.perf_counter()
+        oracle.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                            wl.rotary_dim, wl.slot_mapping, caches, wl.fp8, wl.k_scales,
+                            wl.v_scales, t_begin=t_begin, t_end=t_end)
+        return time.perf_counter() - t0
+
+    # whole-workload calls, repeated until the budget is spent (at least one)
+    reps, total = 0, 0.0
+    while reps == 0 or total < budget_s:
+        total += run(wl.num_ctx)
+        reps += 1
+    nbytes = wl.algorithmic_bytes() * reps
+    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole call(s) of the %s workload (%d tokens), single thread, %.1f s"
+                      % (reps, wl.name, wl.num_ctx, total),
+            "token_layers_per_s": wl.token_layers() * reps / total}
+
+
+def traffic_for(name: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="all", choices=["all"] + W.NAMES)
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated in the timed loop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the write is "
+              "independent per token and per kv head, so ranks would shard without any "
+              "exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    _lib.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+
+    if args.calib_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x %d bytes read + written" % n)
+        del src, dst
+
+    names = W.NAMES if args.workload == "all" else [args.workload]
+    results = {}
+    for name in names:
+        index = W.NAMES.index(name)
+        if index == 0:
+            continue   # the tiny case is a parity case, not a bench line
+        log("workload", name, "setup")
+        if index == 4:
+            setup = Setup(index, 1, dev)
+            r = time_graph(setup, max(args.steps, 1000), args.warmup, stream)
+            per = r["per_call_s"]
+            results[name] = {"us_per_call": per * 1e6, "GB_s": r["bytes"] / per / 1e9,
+                             "token_layers_per_s": r["token_layers"] / per,
+                             "timing": "hipGraph replay of one write, %d replays" % max(args.steps, 1000),
+                             "bytes_per_call": r["bytes"]}
+        else:
+            n_sets = 1 if index == 3 else args.sets
+            setup = Setup(index, n_sets, dev)
+            r = time_eager(setup, args.steps, args.warmup, stream)
+            k = r["kernel_s"]
+            results[name] = {
+                "ms_per_step": r["region_s"] / args.steps * 1e3,
+                "GB_s": float(r["bytes"].sum() / r["region_s"] / 1e9),
+                "kernel_us_mean": float(k.mean() * 1e6),
+                "kernel_us_median": float(np.median(k) * 1e6),
+                "kernel_us_p10": float(np.percentile(k, 10) * 1e6),
+                "kernel_us_p90": float(np.percentile(k, 90) * 1e6),
+                "kernel_GB_s": float(r["bytes"].mean() / k.mean() / 1e9),
+                "token_layers_per_s": float(r["token_layers"].sum() / r["region_s"]),
+                "bytes_per_call": int(r["bytes"].mean()),
+                "input_sets": n_sets,
+                "wall_s": r["wall_s"],
+            }
+        results[name]["pct_of_hbm_peak"] = 100.0 * results[name].get("kernel_GB_s", results[name]["GB_s"]) / HBM_PEAK_GBS
+        log(name, json.dumps(results[name]))
+        del setup
+        torch.cuda.empty_cache()
+
+    head = W.NAMES[HEADLINE]
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+    if head in results:
+        h = results[head]
+        out.update({"value": h["GB_s"], "ms_per_step": h["ms_per_step"],
+                    "token_layers_per_s": h["token_layers_per_s"],
+                    "pct_of_hbm_peak": 100.0 * h["GB_s"] / HBM_PEAK_GBS})
+        out["config"] = {"workload": head + ": " + W.DESCRIPTIONS[HEADLINE],
+                         "num_ctx": 4096, "layers": 5, "kv_heads": 8, "head_dim": 128,
+                         "rotary_dim": 64, "cache": "bf16", "io": "bf16 in, bf16 cache",
+                         "input_sets_rotated": h["input_sets"]}
+        out["roofline"] = {"bound": "hbm", "achieved": h["kernel_GB_s"], "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": h["kernel_GB_s"] / HBM_PEAK_GBS,
+                           "traffic": traffic_for(head),
+                           "kernel": "ctx_kv_write_kernel<64, bf16, 3 layer-pair groups>",
+                           "kernel_us_mean": h["kernel_us_mean"],
+                           "algorithmic_bytes_per_launch": h["bytes_per_call"]}
+    else:
+        name = next(iter(results))
+        out.update({"value": results[name]["GB_s"],
+                    "ms_per_step": results[name].get("ms_per_step", results[name].get("us_per_call", 0) / 1e3)})
+        out["config"] = {"workload": name + ": " + W.DESCRIPTIONS[W.NAMES.index(name)]}
+        out["roofline"] = None
+    out["workloads"] = results
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cb_index = HEADLINE if head in results else W.NAMES.index(next(iter(results)))
+        out["cpu_baseline"] = cpu_baseline(cb_index)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * dspark_ctx_kv.h - C ABI of the DSpark fused context-KV write for MI355X
+ * (gfx950).
+ *
+ * The operation is the one the vLLM API page
+ * "vllm.models.minimax_m3.common.ops.dspark_context_kv" defines in its module
+ * docstring and in class DSparkContextKVWriter: from the fused projection
+ * output all_kv [num_ctx, L, 2, nkv, 128] (bf16), every draft layer l gets
+ *
+ *   K = partial NeoX RoPE( bf16( x * rsqrt(mean(x^2) + eps) * (1 + w_l) ) )
+ *       (the norm in fp32, its output rounded to bf16; RoPE on the leading
+ *        rotary_dim dims at the token's position, each result rounded to bf16)
+ *   V = all_kv[t, l, 1, h, :] unchanged
+ *
+ * stored at cache_l[slot / block_size, h, slot % block_size, 0:128] (K) and
+ * [..., 128:256] (V) of layer l's separately allocated paged cache
+ * [num_blocks, nkv, block_size, 256], as raw bf16 or as OCP fp8 e4m3 of
+ * (fp32 value) / (fp32 per-layer scale), saturating at +-448.  A token whose
+ * slot is < 0 is padding: nothing is read for it and nothing is written.
+ *
+ * The writer is built once from the layers' caches and scales (class
+ * DSparkContextKVWriter.__init__ and _validate on that page).  Layer l's cache
+ * is addressed as layer 0's cache plus a per-layer element offset, and each
+ * scale as layer 0's k scale plus a float offset (_ensure_tables); the offsets
+ * are computed at creation and travel by value in every launch, so a call
+ * captured in a HIP graph keeps addressing the same memory and never needs a
+ * host-to-device copy.
+ *
+ * Ownership: the caller owns every device buffer and stream; the library owns
+ * only the writer object (host memory).  All entry points are thread-safe for
+ * distinct writers; the last-error string is per thread.
+ */
+#ifndef DSPARK_CTX_KV_H
+#define DSPARK_CTX_KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head size the write supports ("2 * 128" cache rows; rotary_dims_supported). */
+#define DSPARK_HEAD_DIM 128
+/* Most draft layers one writer handles (a draft has a handful; the offsets
+ * ride in the kernel-argument segment). */
+#define DSPARK_MAX_LAYERS 32
+
+/* kv_cache_dtype: "auto" (raw bf16 cache) or "fp8" / "fp8_e4m3" (uint8
+ * storage holding OCP e4m3), as accepted by DSparkContextKVWriter. */
+enum {
+    DSPARK_KV_AUTO = 0,
+    DSPARK_KV_FP8_E4M3 = 1
+};
+
+/* Status codes.  On any non-zero status dspark_ctx_kv_last_error() gives the
+ * reason. */
+enum {
+    DSPARK_OK = 0,
+    DSPARK_E_LAYOUT = -1, /* cache layout the writer does not support (_validate) */
+    DSPARK_E_ARG = -2,    /* bad argument to write (shape mismatch, rotary dim, pointer) */
+    DSPARK_E_HIP = -4     /* the HIP runtime reported an error */
+};
+
+typedef struct dspark_ctx_kv_writer dspark_ctx_kv_writer; /* opaque */
+
+/* Host-only check of a cache layout, the rules of
+ * DSparkContextKVWriter._validate as far as raw pointers and sizes carry them
+ * (dtype, contiguity and per-layer shape equality are the caller's: the
+ * Python binding checks them on the tensors):
+ *   num_layers in 1..DSPARK_MAX_LAYERS ("no layers");
+ *   kv_cache_dtype is DSPARK_KV_AUTO or DSPARK_KV_FP8_E4M3;
+ *   every cache pointer non-NULL and num_blocks, num_kv_heads, block_size > 0
+ *     ("KV cache not bound");
+ *   head_dim == 128, i.e. rows of 256 elements ("unexpected cache shape");
+ *   block_size a power of two;
+ *   every k/v scale pointer non-NULL and 4-byte aligned;
+ *   every cache's distance from layer 0's cache a multiple of 16 elements,
+ *     and layer 0's cache 16-byte aligned (16-byte vector stores);
+ *   every scale's distance from layer 0's k scale a multiple of 4 bytes.
+ * kv_caches, k_scales, v_scales are host arrays of num_layers device
+ * pointers.  Touches no device.  Returns DSPARK_OK or DSPARK_E_LAYOUT. */
+int dspark_ctx_kv_validate(int32_t num_layers,
+                           void *const *kv_caches,
+                           const float *const *k_scales,
+                           const float *const *v_scales,
+                           int64_t num_blocks, int32_t num_kv_heads,
+                           int32_t block_size, int32_t head_dim,
+                           int32_t kv_cache_dtype);
+
+/* Build a writer for num_layers caches, each [num_blocks, num_kv_heads,
+ * block_size, 2 * head_dim] of bf16 (DSPARK_KV_AUTO) or uint8
+ * (DSPARK_KV_FP8_E4M3), contiguous.  Validates as dspark_ctx_kv_validate,
+ * then computes the per-layer cache offsets (elements from kv_caches[0]) and
+ * scale offsets (floats from k_scales[0]).  The scale VALUES are read on the
+ * device at every write, so they may change between calls or graph replays;
+ * the cache and scale ADDRESSES may not (destroy and create again to re-bind).
+ * Allocates host memory only.  On success *out receives the writer and the
+ * return is DSPARK_OK; otherwise *out is NULL and the return is
+ * DSPARK_E_LAYOUT or DSPARK_E_ARG (out == NULL). */
+int dspark_ctx_kv_writer_create(int32_t num_layers,
+                                void *const *kv_caches,
+                                const float *const *k_scales,
+                                const float *const *v_scales,
+                                int64_t num_blocks, int32_t num_kv_heads,
+                                int32_t block_size, int32_t head_dim,
+                                int32_t kv_cache_dtype,
+                                dspark_ctx_kv_writer **out);
+
+/* Enqueue the fused write on `stream` (a hipStream_t; NULL = the null
+ * stream).  One kernel launch; no allocation, synchronisation or copy, so the
+ * call can be captured in a HIP graph.  Arguments (device pointers):
+ *   all_kv         bf16 [num_ctx, num_layers, 2, num_kv_heads, 128],
+ *                  contiguous, 16-byte aligned; axis 2: 0 = K, 1 = V
+ *   k_norm_weight  bf16 [num_layers, 128], row l = layer l's K-norm weight w
+ *                  (the norm multiplies by 1 + w), 16-byte aligned
+ *   eps            the norm's epsilon (used as fp32)
+ *   positions      int64 [num_ctx], the row of cos_sin_cache for each token
+ *   cos_sin_cache  bf16 [cos_sin_rows, rotary_dim], row p = [cos | sin] of
+ *                  the rotary_dim/2 frequencies, 16-byte aligned
+ *   rotary_dim     16, 32 or 64 (dspark_rotary_dims_supported)
+ *   slot_mapping   int64 [num_ctx]; < 0 = padding, else the cache slot
+ * num_layers and num_kv_heads must equal the writer's (the assert in
+ * DSparkContextKVWriter.__call__).  num_ctx == 0 returns DSPARK_OK without a
+ * launch.  Preconditions NOT checked on the device (as on the page): every
+ * position of a non-padding token is in [0, cos_sin_rows), every slot is
+ * < num_blocks * block_size, and no two non-padding tokens share a slot
+ * (with duplicates either token's values may land).  The buffers must not be
+ * written by other work while the kernel runs.  Returns DSPARK_OK,
+ * DSPARK_E_ARG or DSPARK_E_HIP (launch failure). */
+int dspark_ctx_kv_writer_write(dspark_ctx_kv_writer *w,
+                               const void *all_kv, int64_t num_ctx,
+                               int32_t num_layers, int32_t num_kv_heads,
+                               const void *k_norm_weight, float eps,
+                               const int64_t *positions,
+                               const void *cos_sin_cache, int64_t cos_sin_rows,
+                               int32_t rotary_dim,
+                               const int64_t *slot_mapping,
+                               void *stream);
+
+/* Free a writer (host memory only).  No graph that captured a write through
+ * it may be replayed afterwards.  NULL is ignored. */
+void dspark_ctx_kv_writer_destroy(dspark_ctx_kv_writer *w);
+
+/* 1 if the write supports this rotary dim and head size (rotary_dims_supported:
+ * the leading 16, 32 or 64 dims of a 128-dim head), else 0. */
+int dspark_rotary_dims_supported(int32_t rotary_dim, int32_t head_dim);
+
+/* The reason for the last non-zero status returned on this thread ("" if
+ * none).  Valid until the next call on this thread. */
+const char *dspark_ctx_kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_CTX_KV_H */

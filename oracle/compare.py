@@ -36,8 +36,8 @@ def ordinal_e4m3(codes: np.ndarray) -> np.ndarray:
 @dataclass
 class PartStats:
     n: int = 0
-    exact: int = 0
-    within1: int = 0       # distance exactly 1 from the oracle's code
+    exact: int = 0         # bit-equal to the oracle's code
+    within1: int = 0       # not bit-equal, ordinal distance <= 1 (+0 vs -0 is 0)
     by_alternate: int = 0  # farther than 1 from the code, within 1 of an alternate
     fail: int = 0
     max_dist: int = 0
@@ -144,8 +144,9 @@ def compare(device_caches, oracle_result, slot_mapping, fp8: bool, sentinel: int
                     stats.max_dist = int(np.abs(ordf(gp[neq]) - ordf(op[neq])).max())
                 continue
             d = np.abs(ordf(gp) - ordf(op))
-            stats.exact = int(np.count_nonzero(d == 0))
-            stats.within1 = int(np.count_nonzero(d == 1))
+            same = gp == op
+            stats.exact = int(np.count_nonzero(same))
+            stats.within1 = int(np.count_nonzero((d <= 1) & ~same))
             far = np.argwhere(d > 1)
             maxd = int(d.max()) if d.size else 0
             for r_i, c_i in far:

@@ -1,0 +1,102 @@
+"""ctypes binding of libdspark_ctx_kv.so (include/dspark_ctx_kv.h).
+
+Argument marshalling only: every function here has the name and argument
+order of the C entry point it calls, takes device pointers as Python ints,
+and returns the C status.  The library must have been built in-tree
+(``python -m speculative_decoding_draft_02_amd.build``); loading fails
+loudly otherwise, and nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark_ctx_kv.so")
+
+HEAD_DIM = 128
+MAX_LAYERS = 32
+KV_AUTO = 0
+KV_FP8_E4M3 = 1
+OK = 0
+E_LAYOUT = -1
+E_ARG = -2
+E_HIP = -4
+
+# every entry point the header declares, with its ctypes signature
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "dspark_ctx_kv_validate": ([_I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32], ctypes.c_int),
+    "dspark_ctx_kv_writer_create": ([_I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_write": ([_P, _P, _I64, _I32, _I32, _P, ctypes.c_float, _P, _P, _I64,
+                                    _I32, _P, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_destroy": ([_P], None),
+    "dspark_rotary_dims_supported": ([_I32, _I32], ctypes.c_int),
+    "dspark_ctx_kv_last_error": ([], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                "libdspark_ctx_kv.so is not built (%s); run "
+                "`python -m speculative_decoding_draft_02_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*[int(p) for p in ptrs])
+
+
+def dspark_ctx_kv_validate(num_layers, kv_caches, k_scales, v_scales, num_blocks,
+                           num_kv_heads, block_size, head_dim, kv_cache_dtype) -> int:
+    return load().dspark_ctx_kv_validate(
+        num_layers, ctypes.cast(_ptr_array(kv_caches), _P), ctypes.cast(_ptr_array(k_scales), _P),
+        ctypes.cast(_ptr_array(v_scales), _P), num_blocks, num_kv_heads, block_size, head_dim,
+        kv_cache_dtype)
+
+
+def dspark_ctx_kv_writer_create(num_layers, kv_caches, k_scales, v_scales, num_blocks,
+                                num_kv_heads, block_size, head_dim, kv_cache_dtype):
+    """Returns (status, writer handle as int or None)."""
+    out = ctypes.c_void_p(0)
+    st = load().dspark_ctx_kv_writer_create(
+        num_layers, ctypes.cast(_ptr_array(kv_caches), _P), ctypes.cast(_ptr_array(k_scales), _P),
+        ctypes.cast(_ptr_array(v_scales), _P), num_blocks, num_kv_heads, block_size, head_dim,
+        kv_cache_dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def dspark_ctx_kv_writer_write(writer, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight,
+                               eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim,
+                               slot_mapping, stream) -> int:
+    return load().dspark_ctx_kv_writer_write(
+        writer, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight, eps, positions,
+        cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)
+
+
+def dspark_ctx_kv_writer_destroy(writer) -> None:
+    load().dspark_ctx_kv_writer_destroy(writer)
+
+
+def dspark_rotary_dims_supported(rotary_dim, head_dim) -> int:
+    return load().dspark_rotary_dims_supported(rotary_dim, head_dim)
+
+
+def dspark_ctx_kv_last_error() -> str:
+    return load().dspark_ctx_kv_last_error().decode()

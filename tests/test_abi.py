@@ -1,0 +1,192 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+the header declares, and its host logic (layout validation with the reasons
+of DSparkContextKVWriter._validate, argument checks of write, the supported
+rotary dims) behaves as documented.  No call here reaches a GPU: create is
+host-only and every write below is refused or is a no-op before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_draft_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark_ctx_kv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from speculative_decoding_draft_02_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared_functions()
+    assert names == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "speculative_decoding_draft_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()
+
+
+@pytest.mark.parametrize("r,hd,ok", [(16, 128, 1), (32, 128, 1), (64, 128, 1), (48, 128, 0),
+                                     (128, 128, 0), (0, 128, 0), (64, 64, 0), (32, 256, 0)])
+def test_rotary_dims_supported(lib, r, hd, ok):
+    assert _lib.dspark_rotary_dims_supported(r, hd) == ok
+
+
+# fake, never dereferenced device addresses (host-only validation)
+BASE = 0x7F0000000000
+
+
+def _layout(L=5, nb=512, nkv=8, bs=64, hd=128, dtype=_lib.KV_AUTO, stride=None, caches=None,
+            ks=None, vs=None):
+    esize = 1 if dtype == _lib.KV_FP8_E4M3 else 2
+    stride = stride if stride is not None else nb * nkv * bs * 2 * hd * esize + 4096
+    caches = caches if caches is not None else [BASE + l * stride for l in range(L)]
+    ks = ks if ks is not None else [0x10000 + 8 * l for l in range(L)]
+    vs = vs if vs is not None else [0x10004 + 8 * l for l in range(L)]
+    return [L, caches, ks, vs, nb, nkv, bs, hd, dtype]
+
+
+def _validate(args):
+    st = _lib.dspark_ctx_kv_validate(*args)
+    return st, _lib.dspark_ctx_kv_last_error() if st else None
+
+
+def test_validate_accepts_the_workload_layouts(lib):
+    assert _validate(_layout())[0] == _lib.OK
+    assert _validate(_layout(dtype=_lib.KV_FP8_E4M3, bs=16, nb=4096))[0] == _lib.OK
+    assert _validate(_layout(L=1, nkv=2, bs=16, nb=8))[0] == _lib.OK
+    # layers may sit below layer 0 (negative offsets)
+    assert _validate(_layout(L=3, caches=[BASE + 4096, BASE, BASE + 8192]))[0] == _lib.OK
+
+
+@pytest.mark.parametrize("mutate,reason", [
+    (lambda a: a.__setitem__(0, 0), "no layers"),
+    (lambda a: a.__setitem__(0, 33), "layers exceed"),
+    (lambda a: a.__setitem__(8, 7), "kv_cache_dtype 7"),
+    (lambda a: a[1].__setitem__(2, 0), "KV cache not bound"),
+    (lambda a: a.__setitem__(4, 0), "KV cache not bound"),
+    (lambda a: a.__setitem__(7, 64), "unexpected cache shape"),
+    (lambda a: a.__setitem__(6, 48), "block size 48 is not a power of two"),
+    (lambda a: a[2].__setitem__(1, 0), "_k_scale is not a device fp32 pointer"),
+    (lambda a: a[3].__setitem__(4, 0x10006), "_v_scale is not a device fp32 pointer"),
+    (lambda a: a[1].__setitem__(3, a[1][3] + 2), "not 16-element aligned to each other"),
+    (lambda a: a[1].__setitem__(0, BASE + 8), "not 16-byte aligned"),
+])
+def test_validate_reasons(lib, mutate, reason):
+    args = _layout()
+    args[1] = list(args[1])
+    args[2] = list(args[2])
+    args[3] = list(args[3])
+    mutate(args)
+    if args[0] > len(args[1]):
+        args[1] = args[1] + [BASE] * (args[0] - len(args[1]))
+        args[2] = args[2] + [0x10000] * (args[0] - len(args[2]))
+        args[3] = args[3] + [0x10000] * (args[0] - len(args[3]))
+    st, why = _validate(args)
+    assert st == _lib.E_LAYOUT
+    assert reason in why
+
+
+def test_fp8_alignment_is_in_elements(lib):
+    # 16 uint8 elements = 16 bytes apart is aligned for fp8 caches, not for bf16
+    caches = [BASE, BASE + 16 * 1000]
+    assert _validate(_layout(L=2, dtype=_lib.KV_FP8_E4M3, caches=caches))[0] == _lib.OK
+    caches = [BASE, BASE + 16 * 1001]
+    assert _validate(_layout(L=2, dtype=_lib.KV_AUTO, caches=caches))[0] == _lib.E_LAYOUT
+
+
+def test_create_write_argument_checks_destroy(lib):
+    st, w = _lib.dspark_ctx_kv_writer_create(*_layout())
+    assert st == _lib.OK and w
+    fake = BASE + 0x100000
+    common = dict(k_norm_weight=fake, eps=1e-6, positions=fake, cos_sin_cache=fake,
+                  cos_sin_rows=4096, slot_mapping=fake, stream=None)
+
+    def write(**kw):
+        args = dict(writer=w, all_kv=fake, num_ctx=16, num_layers=5, num_kv_heads=8,
+                    rotary_dim=64)
+        args.update(common)
+        args.update(kw)
+        return _lib.dspark_ctx_kv_writer_write(
+            args["writer"], args["all_kv"], args["num_ctx"], args["num_layers"],
+            args["num_kv_heads"], args["k_norm_weight"], args["eps"], args["positions"],
+            args["cos_sin_cache"], args["cos_sin_rows"], args["rotary_dim"],
+            args["slot_mapping"], args["stream"])
+
+    assert write(num_layers=4) == _lib.E_ARG
+    assert "built for 5 and 8" in _lib.dspark_ctx_kv_last_error()
+    assert write(num_kv_heads=2) == _lib.E_ARG
+    assert write(rotary_dim=48) == _lib.E_ARG
+    assert "rotary_dim 48" in _lib.dspark_ctx_kv_last_error()
+    assert write(num_ctx=-1) == _lib.E_ARG
+    assert write(all_kv=0) == _lib.E_ARG
+    assert write(all_kv=fake + 8) == _lib.E_ARG
+    assert write(positions=fake + 4) == _lib.E_ARG
+    assert write(cos_sin_rows=0) == _lib.E_ARG
+    assert write(num_ctx=1 << 28) == _lib.E_ARG       # num_ctx * nkv >= 2^31
+    # num_ctx == 0 is a no-op: OK without a launch (and without touching a device)
+    assert write(num_ctx=0) == _lib.OK
+    _lib.dspark_ctx_kv_writer_destroy(w)
+    _lib.dspark_ctx_kv_writer_destroy(None)
+
+
+def test_create_refuses_bad_layout_and_null_out(lib):
+    args = _layout()
+    args[6] = 3
+    st, w = _lib.dspark_ctx_kv_writer_create(*args)
+    assert st == _lib.E_LAYOUT and w is None
+    assert "power of two" in _lib.dspark_ctx_kv_last_error()
+    L = _lib.load()
+    assert L.dspark_ctx_kv_writer_create(5, None, None, None, 1, 1, 1, 128, 0, None) == _lib.E_ARG
+
+
+def test_python_writer_validate_reasons_on_cpu_tensors():
+    """The torch-level rules of _validate run without a GPU."""
+    import torch
+    from speculative_decoding_draft_02_amd.writer import AttnLayer, DSparkContextKVWriter
+    cache = torch.zeros(4, 2, 16, 256, dtype=torch.bfloat16)
+    sc = torch.ones(1)
+    V = DSparkContextKVWriter._validate
+    assert V([]) == "no layers"
+    assert V([AttnLayer(cache, sc, sc, "int8")]) == "kv_cache_dtype 'int8'"
+    assert V([AttnLayer(torch.zeros(0), sc, sc)]) == "KV cache not bound"
+    assert V([AttnLayer(torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16), sc, sc)]).startswith(
+        "unexpected cache shape")
+    assert V([AttnLayer(torch.zeros(4, 2, 12, 256, dtype=torch.bfloat16), sc, sc)]) == \
+        "block size 12 is not a power of two"
+    assert V([AttnLayer(cache.transpose(1, 2), sc, sc)]) == "cache is not contiguous"
+    assert V([AttnLayer(cache, sc, sc, "fp8")]) == "fp8 cache has dtype torch.bfloat16"
+    assert V([AttnLayer(cache.view(torch.int16), sc, sc)]) == "cache has dtype torch.int16"
+    assert V([AttnLayer(cache, sc, sc)]) == "_k_scale is not a CUDA fp32 tensor"
+    with pytest.raises(ValueError, match="unsupported DSpark context-KV layout: no layers"):
+        DSparkContextKVWriter([])
