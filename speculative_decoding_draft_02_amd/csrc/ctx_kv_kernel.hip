@@ -25,15 +25,17 @@
 //   * the 128-wide sum of squares is reduced inside the 16-lane row with four
 //     DPP adds (no LDS); every lane ends with the same bits;
 //   * the RoPE partner of element i (i + R/2) sits in the same register of
-//     lane c ^ (R/16), fetched with DPP;
+//     lane c ^ (R/16), fetched with one DPP move (R = 16, 32) or ds_swizzle
+//     (R = 64);
 //   * the token's cos/sin values are loaded once per row into registers and
 //     reused for every layer;
 //   * fp8: x / scale is formed from y = RN(1/scale) (one IEEE division per
 //     wave gives every layer's reciprocals, one per lane) as q0 = x y,
 //     r = fma(q0, scale, -x), q = fma(-r, y, q0), which is the correctly
 //     rounded quotient for every finite bf16 x at the e4m3 resolution
-//     (Markstein's correction step); then clamp to +-448 and the hardware
-//     pack conversion v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950).
+//     (Markstein's correction step) on x clamped to +-460 scale, which also
+//     keeps the result inside the e4m3 range; then the hardware pack
+//     conversion v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,8 +60,6 @@ constexpr int kNumXcds = 8;
 // DPP control codes (CDNA3/CDNA4 ISA, DPP_CTRL field).
 constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowShl4 = 0x104;       // lane i <- lane i + 4 within the row
-constexpr int kRowShr4 = 0x114;       // lane i <- lane i - 4 within the row
 constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i
 constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i within each half row
 
@@ -92,9 +92,10 @@ __device__ __forceinline__ uint32_t rope_partner(uint32_t v, int c) {
     } else if constexpr (R == 32) {
         return dpp_u32<kQuadXor2>(v);
     } else {
-        const uint32_t up = dpp_u32<kRowShl4>(v);
-        const uint32_t dn = dpp_u32<kRowShr4>(v);
-        return (c & 4) ? dn : up;
+        // lane ^ 4 within 32 lanes: ds_swizzle bit mode (and 0x1f, or 0,
+        // xor 4); it runs in the LDS crossbar, not the VALU
+        (void)c;
+        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));
     }
 }
 
@@ -158,28 +159,26 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-__device__ __forceinline__ float clampf(float x, float lim) {
-    return __builtin_fminf(__builtin_fmaxf(x, -lim), lim);
-}
-
-// fp32 quotient x / s rounded as IEEE division would be wherever it can
-// change an e4m3 code, given y = RN(1 / s) (Markstein's correction step with
-// the residual negated, so that +-0 keep their sign).  q0 is clamped to the
-// e4m3 range first: a huge x cannot turn the correction into inf - inf, and a
-// quotient beyond 448 saturates either way.
-__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
-    const float q0 = clampf(x * y, 448.0f);
-    const float rn = __builtin_fmaf(q0, s, -x);
+// fp32 quotient x / s rounded as IEEE division would, given y = RN(1 / s)
+// (Markstein's correction step, residual negated so that +-0 keep their
+// sign).  x is first clamped to +-lim = +-460 s: a quotient at or beyond that
+// stores 448 either way, the clamped quotient stays below 464 so the e4m3
+// conversion cannot overflow (no separate saturation needed), and x y cannot
+// reach infinity.
+__device__ __forceinline__ float div_by_scale(float x, float s, float y, float lim) {
+    const float xc = __builtin_amdgcn_fmed3f(x, -lim, lim);
+    const float q0 = xc * y;
+    const float rn = __builtin_fmaf(q0, s, -xc);
     return __builtin_fmaf(-rn, y, q0);
 }
 
 // 8 bf16 (packed in 4 words) -> 8 OCP e4m3 bytes of value / s.
-__device__ __forceinline__ uint2 pack_fp8(const uint32_t (&b)[4], float s, float y) {
+__device__ __forceinline__ uint2 pack_fp8(const uint32_t (&b)[4], float s, float y, float lim) {
     float v[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        v[2 * k] = clampf(div_by_scale(bf16_lo(b[k]), s, y), 448.0f);
-        v[2 * k + 1] = clampf(div_by_scale(bf16_hi(b[k]), s, y), 448.0f);
+        v[2 * k] = div_by_scale(bf16_lo(b[k]), s, y, lim);
+        v[2 * k + 1] = div_by_scale(bf16_hi(b[k]), s, y, lim);
     }
     int w0 = 0, w1 = 0;
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], w0, false);
@@ -366,8 +365,8 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
                 const float ks = lane_value(my_scale, 2 * j), kr = lane_value(my_rcp, 2 * j);
                 const float vs = lane_value(my_scale, 2 * j + 1), vr = lane_value(my_rcp, 2 * j + 1);
                 const uint32_t vb[4] = {dv[j].x, dv[j].y, dv[j].z, dv[j].w};
-                const uint2 ko = pack_fp8(kb, ks, kr);
-                const uint2 vo = pack_fp8(vb, vs, vr);
+                const uint2 ko = pack_fp8(kb, ks, kr, 460.0f * ks);
+                const uint2 vo = pack_fp8(vb, vs, vr, 460.0f * vs);
                 uint8_t *cache = static_cast<uint8_t *>(a.cache0) + base;
                 store_row8(cache, ko);
                 store_row8(cache + DSPARK_HEAD_DIM, vo);
