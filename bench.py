@@ -20,6 +20,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -63,9 +64,12 @@ def bf16_dev(bits, dev):
 class Setup:
     """Caches + writer for a workload shape, and `n_sets` input sets."""
 
-    def __init__(self, index: int, n_sets: int, dev):
+    def __init__(self, index: int, n_sets: int, dev, layer_slots: bool = False):
         self.index = index
         self.sets = [W.make(index, variant=v) for v in range(n_sets)]
+        if layer_slots:
+            self.sets = [W.per_layer_slots(s, seed=77 + v, pad_fraction=0.02)
+                         for v, s in enumerate(self.sets)]
         wl = self.sets[0]
         self.wl = wl
         layers = []
@@ -90,16 +94,25 @@ class Setup:
         i0 = self.inputs[0]
         self.writer(i0["all_kv"], i0["w"], wl.eps, i0["positions"], i0["cos_sin"],
                     wl.rotary_dim, i0["slots"])
+        self.layer_slots = layer_slots
         torch.cuda.synchronize()
         self.handle = self.writer._handle
         self.bytes = [s.algorithmic_bytes() for s in self.sets]
         self.token_layers = [s.token_layers() for s in self.sets]
         # C-ABI argument tuples, built once: the timed loop only calls
-        self._write = _lib.load().dspark_ctx_kv_writer_write
+        lib = _lib.load()
+        if layer_slots:
+            self._write = lib.dspark_ctx_kv_writer_write_layer_slots
+            self._tables = [(ctypes.c_void_p * wl.num_layers)(
+                *[i["slots"][l].data_ptr() for l in range(wl.num_layers)]) for i in self.inputs]
+            slot_args = [ctypes.cast(t, ctypes.c_void_p) for t in self._tables]
+        else:
+            self._write = lib.dspark_ctx_kv_writer_write
+            slot_args = [i["slots"].data_ptr() for i in self.inputs]
         self._args = [(self.handle, i["all_kv"].data_ptr(), wl.num_ctx, wl.num_layers,
                        wl.num_kv_heads, i["w"].data_ptr(), wl.eps, i["positions"].data_ptr(),
-                       i["cos_sin"].data_ptr(), i["cos_sin"].shape[0], wl.rotary_dim,
-                       i["slots"].data_ptr()) for i in self.inputs]
+                       i["cos_sin"].data_ptr(), i["cos_sin"].shape[0], wl.rotary_dim, sa)
+                      for i, sa in zip(self.inputs, slot_args)]
 
     def launch(self, k: int, stream_ptr) -> None:
         """One write of input set k % n through the C ABI (the same tensors
@@ -312,6 +325,25 @@ def main():
             }
         results[name]["pct_of_hbm_peak"] = 100.0 * results[name].get("kernel_GB_s", results[name]["GB_s"]) / HBM_PEAK_GBS
         log(name, json.dumps(results[name]))
+        del setup
+        torch.cuda.empty_cache()
+
+    if args.workload in ("all", "prefill_bf16"):
+        # the prefill shape with one slot mapping per layer (layers in
+        # different KV-cache groups), through the per-layer entry point
+        log("workload prefill_bf16_layer_slots setup")
+        setup = Setup(HEADLINE, args.sets, dev, layer_slots=True)
+        r = time_eager(setup, args.steps, args.warmup, stream)
+        avg = r["region_s"] / args.steps
+        results["prefill_bf16_layer_slots"] = {
+            "ms_per_step": avg * 1e3, "GB_s": float(r["bytes"].sum() / r["region_s"] / 1e9),
+            "kernel_us_avg": avg * 1e6, "kernel_GB_s": float(r["bytes"].mean() / avg / 1e9),
+            "token_layers_per_s": float(r["token_layers"].sum() / r["region_s"]),
+            "bytes_per_call": int(r["bytes"].mean()), "input_sets": args.sets,
+            "note": "per-layer block tables, 2% padding per layer"}
+        results["prefill_bf16_layer_slots"]["pct_of_hbm_peak"] = \
+            100.0 * results["prefill_bf16_layer_slots"]["kernel_GB_s"] / HBM_PEAK_GBS
+        log("prefill_bf16_layer_slots", json.dumps(results["prefill_bf16_layer_slots"]))
         del setup
         torch.cuda.empty_cache()
 

@@ -16,7 +16,8 @@
  * [..., 128:256] (V) of layer l's separately allocated paged cache
  * [num_blocks, nkv, block_size, 256], as raw bf16 or as OCP fp8 e4m3 of
  * (fp32 value) / (fp32 per-layer scale), saturating at +-448.  A token whose
- * slot is < 0 is padding: nothing is read for it and nothing is written.
+ * slot is < 0 is padding: nothing is written for it (its rows may still be
+ * read, which the kernel does ahead of the slot to hide the slot's latency).
  *
  * The writer is built once from the layers' caches and scales (class
  * DSparkContextKVWriter.__init__ and _validate on that page).  Layer l's cache
@@ -136,6 +137,27 @@ int dspark_ctx_kv_writer_write(dspark_ctx_kv_writer *w,
                                int32_t rotary_dim,
                                const int64_t *slot_mapping,
                                void *stream);
+
+/* The same write when every draft layer has its own slot mapping (layers in
+ * different KV-cache groups): the case the vLLM API page
+ * "vllm.models.minimax_m3.common.dspark" (_shared_slot_mapping) sends to the
+ * unfused path, because its fused kernel takes one mapping for all layers.
+ * slot_mappings is a host array of num_layers device pointers, each int64
+ * [num_ctx], 8-byte aligned; layer l's K and V rows of token t go to
+ * slot_mappings[l][t], and a slot < 0 skips that layer only (the token's rows
+ * are still read).  Everything else, including the preconditions, is as for
+ * dspark_ctx_kv_writer_write; the pointers are taken by value into the
+ * launch, so the host array may be reused after the call.  Returns DSPARK_OK,
+ * DSPARK_E_ARG (also for a NULL or misaligned mapping) or DSPARK_E_HIP. */
+int dspark_ctx_kv_writer_write_layer_slots(dspark_ctx_kv_writer *w,
+                                           const void *all_kv, int64_t num_ctx,
+                                           int32_t num_layers, int32_t num_kv_heads,
+                                           const void *k_norm_weight, float eps,
+                                           const int64_t *positions,
+                                           const void *cos_sin_cache,
+                                           int64_t cos_sin_rows, int32_t rotary_dim,
+                                           const int64_t *const *slot_mappings,
+                                           void *stream);
 
 /* Free a writer (host memory only).  No graph that captured a write through
  * it may be replayed afterwards.  NULL is ignored. */

@@ -67,7 +67,7 @@ def lib():
             P, i64, i32, i32,            # all_kv, num_ctx, L, nkv
             P, ctypes.c_float,           # k_norm_weight, eps
             P, P, i64, i32,              # positions, cos_sin, cs_rows, R
-            P, i64, i32,                 # slots, num_blocks, block_size
+            P, i64, i64, i32,            # slots, slot_layer_stride, num_blocks, block_size
             i32, P, P,                   # fp8, k_scales, v_scales
             P,                           # caches (void**)
             ctypes.c_double,             # near_delta
@@ -125,7 +125,8 @@ def ctx_kv_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim,
     written in place and returned; every other input is read only.
 
     all_kv: uint16 [num_ctx, L, 2, nkv, 128]; k_norm_weight: uint16 [L, 128];
-    positions, slot_mapping: int64 [num_ctx]; cos_sin: uint16 [rows, R];
+    positions: int64 [num_ctx]; slot_mapping: int64 [num_ctx] (shared by every
+    layer) or [L, num_ctx] (one mapping per layer); cos_sin: uint16 [rows, R];
     k_scales, v_scales: float32 [L].
     """
     all_kv = np.ascontiguousarray(all_kv, dtype=np.uint16)
@@ -143,6 +144,12 @@ def ctx_kv_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim,
         assert c.dtype == want and c.flags.c_contiguous and c.ndim == 4
         assert c.shape == caches[0].shape and c.shape[1] == nkv and c.shape[3] == 2 * HEAD_DIM
     num_blocks, _, bs, _ = caches[0].shape
+    if slots.ndim == 2:
+        assert slots.shape == (L, num_ctx)
+        slot_stride = num_ctx
+    else:
+        assert slots.shape == (num_ctx,)
+        slot_stride = 0
     ks = np.ascontiguousarray(k_scales if k_scales is not None else np.ones(L), dtype=np.float32)
     vs = np.ascontiguousarray(v_scales if v_scales is not None else np.ones(L), dtype=np.float32)
     if t_end is None:
@@ -158,7 +165,7 @@ def ctx_kv_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim,
         n = lib().dspark_oracle_ctx_kv_write(
             all_kv.ctypes.data, num_ctx, L, nkv, w.ctypes.data, float(eps),
             pos.ctypes.data, cs.ctypes.data, cs.shape[0], rotary_dim,
-            slots.ctypes.data, num_blocks, bs, 1 if fp8 else 0,
+            slots.ctypes.data, slot_stride, num_blocks, bs, 1 if fp8 else 0,
             ks.ctypes.data, vs.ctypes.data, ctypes.cast(ptrs, ctypes.c_void_p),
             float(near_delta), a_layer.ctypes.data, a_index.ctypes.data,
             a_count.ctypes.data, a_codes.ctypes.data, cap, t_begin, t_end)

@@ -103,16 +103,19 @@ def written_rows(slot_mapping: np.ndarray, nkv: int, block_size: int) -> np.ndar
 def compare(device_caches, oracle_result, slot_mapping, fp8: bool, sentinel: int,
             block_size: int | None = None) -> Report:
     """Compare device caches (numpy, same dtype/shape as the oracle's) with
-    the oracle's caches and alternates.  ``sentinel`` is the byte/element
+    the oracle's caches and alternates.  ``slot_mapping`` is [num_ctx]
+    (shared) or [L, num_ctx] (per layer).  ``sentinel`` is the byte/element
     value every cache held before the call."""
     oc = oracle_result.caches
     L = len(oc)
     nkv = oc[0].shape[1]
     bs = oc[0].shape[2] if block_size is None else block_size
-    rows = written_rows(slot_mapping, nkv, bs)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    per_layer = slots.ndim == 2          # [L, num_ctx]: one mapping per layer
     ordf = ordinal_e4m3 if fp8 else ordinal_bf16
     layers = []
     for l in range(L):
+        rows = written_rows(slots[l] if per_layer else slots, nkv, bs)
         rep = LayerReport()
         dev = np.asarray(device_caches[l]).reshape(-1, 256)
         ora = oc[l].reshape(-1, 256)

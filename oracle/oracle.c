@@ -196,7 +196,10 @@ static int add_candidate(uint16_t *set, int n, uint16_t c)
  * eps            the norm epsilon, as fp32
  * positions      int64 [num_ctx]
  * cos_sin        bf16 bits [cs_rows, R], row p = [cos(p*theta_i) | sin(...)]
- * slot_mapping   int64 [num_ctx]; < 0 is padding
+ * slot_mapping   int64; layer l uses slot_mapping[l * slot_layer_stride + t]:
+ *                stride 0 = one mapping [num_ctx] shared by every layer, stride
+ *                num_ctx = one mapping per layer [L, num_ctx] (draft layers in
+ *                different KV-cache groups); < 0 is padding for that layer
  * caches         L host pointers, each [num_blocks, nkv, bs, 256] of uint16
  *                (bf16 cache) or uint8 (fp8 cache)
  * k_scales, v_scales  fp32 [L] (read only for fp8 caches)
@@ -216,7 +219,8 @@ int64_t dspark_oracle_ctx_kv_write(
     const uint16_t *k_norm_weight, float eps,
     const int64_t *positions, const uint16_t *cos_sin, int64_t cs_rows,
     int32_t rotary_dim,
-    const int64_t *slot_mapping, int64_t num_blocks, int32_t block_size,
+    const int64_t *slot_mapping, int64_t slot_layer_stride,
+    int64_t num_blocks, int32_t block_size,
     int32_t fp8, const float *k_scales, const float *v_scales,
     void *const *caches,
     double near_delta,
@@ -243,19 +247,19 @@ int64_t dspark_oracle_ctx_kv_write(
     uint16_t kcode[HEAD_DIM];
 
     for (int64_t t = t_begin; t < t_end; ++t) {
-        int64_t slot = slot_mapping[t];
-        if (slot < 0)
-            continue;                               /* padding: not written */
-        if (slot >= num_blocks * (int64_t)block_size)
-            return -4;
-        int64_t blk = slot / block_size;
-        int64_t off = slot % block_size;
-        int64_t p = positions[t];
-        if (p < 0 || p >= cs_rows)
-            return -3;
-        const uint16_t *cs_row = cos_sin + p * R;   /* same row for every layer */
-
         for (int l = 0; l < num_layers; ++l) {
+            int64_t slot = slot_mapping[l * slot_layer_stride + t];
+            if (slot < 0)
+                continue;                           /* padding: not written */
+            if (slot >= num_blocks * (int64_t)block_size)
+                return -4;
+            int64_t blk = slot / block_size;
+            int64_t off = slot % block_size;
+            int64_t p = positions[t];
+            if (p < 0 || p >= cs_rows)
+                return -3;
+            const uint16_t *cs_row = cos_sin + p * R;   /* same row for every layer */
+
             for (int h = 0; h < nkv; ++h) {
                 const uint16_t *krow =
                     all_kv + (((t * num_layers + l) * 2 + 0) * nkv + h) * HEAD_DIM;

@@ -31,6 +31,8 @@ SIGNATURES = {
     "dspark_ctx_kv_writer_create": ([_I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P], ctypes.c_int),
     "dspark_ctx_kv_writer_write": ([_P, _P, _I64, _I32, _I32, _P, ctypes.c_float, _P, _P, _I64,
                                     _I32, _P, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_write_layer_slots": ([_P, _P, _I64, _I32, _I32, _P, ctypes.c_float, _P, _P,
+                                                _I64, _I32, _P, _P], ctypes.c_int),
     "dspark_ctx_kv_writer_destroy": ([_P], None),
     "dspark_rotary_dims_supported": ([_I32, _I32], ctypes.c_int),
     "dspark_ctx_kv_last_error": ([], ctypes.c_char_p),
@@ -88,6 +90,16 @@ def dspark_ctx_kv_writer_write(writer, all_kv, num_ctx, num_layers, num_kv_heads
     return load().dspark_ctx_kv_writer_write(
         writer, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight, eps, positions,
         cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)
+
+
+def dspark_ctx_kv_writer_write_layer_slots(writer, all_kv, num_ctx, num_layers, num_kv_heads,
+                                           k_norm_weight, eps, positions, cos_sin_cache,
+                                           cos_sin_rows, rotary_dim, slot_mappings, stream) -> int:
+    """slot_mappings: a sequence of num_layers device pointers."""
+    return load().dspark_ctx_kv_writer_write_layer_slots(
+        writer, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight, eps, positions,
+        cos_sin_cache, cos_sin_rows, rotary_dim,
+        ctypes.cast(_ptr_array(slot_mappings), _P), stream)
 
 
 def dspark_ctx_kv_writer_destroy(writer) -> None:

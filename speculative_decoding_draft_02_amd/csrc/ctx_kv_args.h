@@ -30,6 +30,10 @@ struct CtxKvArgs {
     int64_t cache_off[DSPARK_MAX_LAYERS];  // elements from cache0
     int64_t kscale_off[DSPARK_MAX_LAYERS]; // floats from scale0
     int64_t vscale_off[DSPARK_MAX_LAYERS]; // floats from scale0
+    // per-layer slot mappings (layer l's [num_ctx] mapping), used instead of
+    // `slots` when layer_slots_on is set
+    const int64_t *layer_slots[DSPARK_MAX_LAYERS];
+    int32_t layer_slots_on;
 };
 
 // Enqueue one launch.  Returns the hipError_t of the launch.

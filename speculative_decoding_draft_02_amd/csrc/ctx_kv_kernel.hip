@@ -228,7 +228,9 @@ __device__ __forceinline__ void norm_rope(const uint4 &d, const uint4 &w, float 
 // in chunks of kChunk.
 // kUniform: nkv % 4 == 0, so a wave's 4 rows are 4 heads of one token and the
 // token's slot and position are wave-uniform (scalar loads, scalar exit).
-template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform>
+// kLayerSlots: every layer has its own slot mapping (layers in different KV
+// cache groups); always with the general row mapping.
+template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform, bool kLayerSlots>
 __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKvArgs a) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4;        // quarter: which of the wave's 4 rows
@@ -251,6 +253,8 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
     int h;
     int64_t slot, pos;
     uint4 dk[kChunk], dv[kChunk], wv[kChunk];
+    int64_t lslot[kChunk];          // per-layer slots (kLayerSlots only)
+    bool in_range = true;
     const int64_t kv_stride = static_cast<int64_t>(nkv) * 16;    // K_l -> V_l (uint4 units)
     const uint4 *w_base = reinterpret_cast<const uint4 *>(a.k_norm_weight) + c;
     const uint4 *kv_base;
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
             dk[j] = load_row16(kv_base + (2 * l) * kv_stride);
             dv[j] = load_row16(kv_base + (2 * l + 1) * kv_stride);
             wv[j] = w_base[l * 16];
+            if constexpr (kLayerSlots) lslot[j] = a.layer_slots[l][t];
         }
     };
     if constexpr (kUniform) {
@@ -281,9 +286,23 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
         // padding: nothing written (a negative position never occurs; testing
         // it keeps both scalar loads ahead of the branch)
         if (slot < 0 || pos < 0) return;
+    } else if constexpr (kLayerSlots) {
+        // Each layer's store has its own slot: every in-range quarter reads
+        // its rows (a quarter past the end reads the wave's first row) and
+        // each layer's stores are predicated on that layer's slot.
+        const uint32_t unit = unit0 + q;                    // (token, kv head) row
+        in_range = unit < a.num_units;
+        t = (in_range ? unit : unit0) / static_cast<uint32_t>(nkv);
+        h = static_cast<int>((in_range ? unit : unit0) - t * static_cast<uint32_t>(nkv));
+        slot = 0;
+        pos = a.positions[t];
+        kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
+                  (static_cast<int64_t>(t) * L * 2 * nkv + h) * 16 + c;
+        load_chunk(0);
+        asm volatile("" ::: "memory");   // keep the loads ahead of the predicated stores
     } else {
         const uint32_t unit = unit0 + q;                    // (token, kv head) row
-        const bool in_range = unit < a.num_units;
+        in_range = unit < a.num_units;
         t = (in_range ? unit : unit0) / static_cast<uint32_t>(nkv);
         h = static_cast<int>((in_range ? unit : unit0) - t * static_cast<uint32_t>(nkv));
         slot = a.slots[t];
@@ -356,11 +375,22 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
             if (l >= L) break;
             uint32_t kb[4];
             norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb);
-            const int64_t base = a.cache_off[l] + row;
+            int64_t base = a.cache_off[l] + row;
+            bool store = true;
+            if constexpr (kLayerSlots) {
+                const int64_t s = lslot[j];
+                store = in_range && s >= 0;
+                const int64_t lb_blk = s >> a.bs_log2;
+                const int64_t lb_off = s & ((int64_t{1} << a.bs_log2) - 1);
+                base = a.cache_off[l] +
+                       ((((lb_blk * nkv + h) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM)) + c * 8;
+            }
             if constexpr (!kFp8) {
                 uint16_t *cache = static_cast<uint16_t *>(a.cache0) + base;
-                store_row16(cache, make_uint4(kb[0], kb[1], kb[2], kb[3]));
-                store_row16(cache + DSPARK_HEAD_DIM, dv[j]);
+                if (store) {
+                    store_row16(cache, make_uint4(kb[0], kb[1], kb[2], kb[3]));
+                    store_row16(cache + DSPARK_HEAD_DIM, dv[j]);
+                }
             } else {
                 const float ks = lane_value(my_scale, 2 * j), kr = lane_value(my_rcp, 2 * j);
                 const float vs = lane_value(my_scale, 2 * j + 1), vr = lane_value(my_rcp, 2 * j + 1);
@@ -368,8 +398,10 @@ __global__ __launch_bounds__(kBlockThreads) void ctx_kv_write_kernel(const CtxKv
                 const uint2 ko = pack_fp8(kb, ks, kr, 460.0f * ks);
                 const uint2 vo = pack_fp8(vb, vs, vr, 460.0f * vs);
                 uint8_t *cache = static_cast<uint8_t *>(a.cache0) + base;
-                store_row8(cache, ko);
-                store_row8(cache + DSPARK_HEAD_DIM, vo);
+                if (store) {
+                    store_row8(cache, ko);
+                    store_row8(cache + DSPARK_HEAD_DIM, vo);
+                }
             }
         }
         if constexpr (kSinglePass) {
@@ -386,11 +418,14 @@ template <int R, bool kFp8, int kChunk, bool kSinglePass>
 void launch_one(const CtxKvArgs &a, hipStream_t stream) {
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (a.nkv % kRowsPerWave == 0)
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true>), grid,
+    if (a.layer_slots_on)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, true>), grid,
+                           dim3(kBlockThreads), 0, stream, a);
+    else if (a.nkv % kRowsPerWave == 0)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, false>), grid,
                            dim3(kBlockThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false>), grid,
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, false>), grid,
                            dim3(kBlockThreads), 0, stream, a);
 }
 

@@ -95,6 +95,74 @@ int validate(int32_t num_layers, void *const *kv_caches, const float *const *k_s
     return ok();
 }
 
+int write_impl(dspark_ctx_kv_writer *w, const void *all_kv, int64_t num_ctx, int32_t num_layers,
+               int32_t num_kv_heads, const void *k_norm_weight, float eps,
+               const int64_t *positions, const void *cos_sin_cache, int64_t cos_sin_rows,
+               int32_t rotary_dim, const int64_t *slot_mapping,
+               const int64_t *const *layer_slot_mappings, void *stream) {
+    if (w == nullptr)
+        return fail(DSPARK_E_ARG, "writer is NULL");
+    if (num_layers != w->num_layers || num_kv_heads != w->num_kv_heads)
+        return fail(DSPARK_E_ARG,
+                    "all_kv has %d layers and %d kv heads; the writer was built for %d and %d",
+                    num_layers, num_kv_heads, w->num_layers, w->num_kv_heads);
+    if (!dspark_rotary_dims_supported(rotary_dim, DSPARK_HEAD_DIM))
+        return fail(DSPARK_E_ARG, "rotary_dim %d is not 16, 32 or 64", rotary_dim);
+    if (num_ctx < 0)
+        return fail(DSPARK_E_ARG, "num_ctx %lld is negative", (long long)num_ctx);
+    if (num_ctx == 0)
+        return ok();
+    if (num_ctx * num_kv_heads >= (int64_t{1} << 31))
+        return fail(DSPARK_E_ARG, "num_ctx * num_kv_heads = %lld exceeds 2^31 - 1",
+                    (long long)(num_ctx * num_kv_heads));
+    if (all_kv == nullptr || k_norm_weight == nullptr || positions == nullptr ||
+        cos_sin_cache == nullptr || (slot_mapping == nullptr && layer_slot_mappings == nullptr))
+        return fail(DSPARK_E_ARG, "a device pointer is NULL");
+    if (layer_slot_mappings != nullptr) {
+        for (int l = 0; l < num_layers; ++l) {
+            if (layer_slot_mappings[l] == nullptr)
+                return fail(DSPARK_E_ARG, "slot mapping of layer %d is NULL", l);
+            if (reinterpret_cast<uintptr_t>(layer_slot_mappings[l]) & 7)
+                return fail(DSPARK_E_ARG, "slot mapping of layer %d is not 8-byte aligned", l);
+        }
+    }
+    if ((reinterpret_cast<uintptr_t>(all_kv) | reinterpret_cast<uintptr_t>(k_norm_weight) |
+         reinterpret_cast<uintptr_t>(cos_sin_cache)) & 15)
+        return fail(DSPARK_E_ARG, "all_kv, k_norm_weight and cos_sin_cache must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(positions) | reinterpret_cast<uintptr_t>(slot_mapping)) & 7)
+        return fail(DSPARK_E_ARG, "positions and slot_mapping must be 8-byte aligned");
+    if (cos_sin_rows <= 0)
+        return fail(DSPARK_E_ARG, "cos_sin_cache has no rows");
+
+    dspark::CtxKvArgs a;
+    memset(&a, 0, sizeof a);
+    a.all_kv = all_kv;
+    a.k_norm_weight = k_norm_weight;
+    a.cos_sin = static_cast<const uint16_t *>(cos_sin_cache);
+    a.positions = positions;
+    a.slots = slot_mapping;
+    a.cache0 = w->cache0;
+    a.scale0 = w->scale0;
+    a.num_units = static_cast<uint32_t>(num_ctx * num_kv_heads);
+    a.num_layers = w->num_layers;
+    a.nkv = w->num_kv_heads;
+    a.bs_log2 = w->bs_log2;
+    a.eps = eps;
+    memcpy(a.cache_off, w->cache_off, sizeof a.cache_off);
+    memcpy(a.kscale_off, w->kscale_off, sizeof a.kscale_off);
+    memcpy(a.vscale_off, w->vscale_off, sizeof a.vscale_off);
+    if (layer_slot_mappings != nullptr) {
+        a.layer_slots_on = 1;
+        for (int l = 0; l < num_layers; ++l) a.layer_slots[l] = layer_slot_mappings[l];
+    }
+
+    const hipError_t e = dspark::launch_ctx_kv(a, rotary_dim, w->kv_cache_dtype == DSPARK_KV_FP8_E4M3,
+                                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DSPARK_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,55 +215,23 @@ int dspark_ctx_kv_writer_write(dspark_ctx_kv_writer *w, const void *all_kv, int6
                                const void *k_norm_weight, float eps, const int64_t *positions,
                                const void *cos_sin_cache, int64_t cos_sin_rows,
                                int32_t rotary_dim, const int64_t *slot_mapping, void *stream) {
-    if (w == nullptr)
-        return fail(DSPARK_E_ARG, "writer is NULL");
-    if (num_layers != w->num_layers || num_kv_heads != w->num_kv_heads)
-        return fail(DSPARK_E_ARG,
-                    "all_kv has %d layers and %d kv heads; the writer was built for %d and %d",
-                    num_layers, num_kv_heads, w->num_layers, w->num_kv_heads);
-    if (!dspark_rotary_dims_supported(rotary_dim, DSPARK_HEAD_DIM))
-        return fail(DSPARK_E_ARG, "rotary_dim %d is not 16, 32 or 64", rotary_dim);
-    if (num_ctx < 0)
-        return fail(DSPARK_E_ARG, "num_ctx %lld is negative", (long long)num_ctx);
-    if (num_ctx == 0)
-        return ok();
-    if (num_ctx * num_kv_heads >= (int64_t{1} << 31))
-        return fail(DSPARK_E_ARG, "num_ctx * num_kv_heads = %lld exceeds 2^31 - 1",
-                    (long long)(num_ctx * num_kv_heads));
-    if (all_kv == nullptr || k_norm_weight == nullptr || positions == nullptr ||
-        cos_sin_cache == nullptr || slot_mapping == nullptr)
+    if (slot_mapping == nullptr && num_ctx > 0)
         return fail(DSPARK_E_ARG, "a device pointer is NULL");
-    if ((reinterpret_cast<uintptr_t>(all_kv) | reinterpret_cast<uintptr_t>(k_norm_weight) |
-         reinterpret_cast<uintptr_t>(cos_sin_cache)) & 15)
-        return fail(DSPARK_E_ARG, "all_kv, k_norm_weight and cos_sin_cache must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(positions) | reinterpret_cast<uintptr_t>(slot_mapping)) & 7)
-        return fail(DSPARK_E_ARG, "positions and slot_mapping must be 8-byte aligned");
-    if (cos_sin_rows <= 0)
-        return fail(DSPARK_E_ARG, "cos_sin_cache has no rows");
+    return write_impl(w, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight, eps, positions,
+                      cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, nullptr, stream);
+}
 
-    dspark::CtxKvArgs a;
-    memset(&a, 0, sizeof a);
-    a.all_kv = all_kv;
-    a.k_norm_weight = k_norm_weight;
-    a.cos_sin = static_cast<const uint16_t *>(cos_sin_cache);
-    a.positions = positions;
-    a.slots = slot_mapping;
-    a.cache0 = w->cache0;
-    a.scale0 = w->scale0;
-    a.num_units = static_cast<uint32_t>(num_ctx * num_kv_heads);
-    a.num_layers = w->num_layers;
-    a.nkv = w->num_kv_heads;
-    a.bs_log2 = w->bs_log2;
-    a.eps = eps;
-    memcpy(a.cache_off, w->cache_off, sizeof a.cache_off);
-    memcpy(a.kscale_off, w->kscale_off, sizeof a.kscale_off);
-    memcpy(a.vscale_off, w->vscale_off, sizeof a.vscale_off);
-
-    const hipError_t e = dspark::launch_ctx_kv(a, rotary_dim, w->kv_cache_dtype == DSPARK_KV_FP8_E4M3,
-                                               static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(DSPARK_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+int dspark_ctx_kv_writer_write_layer_slots(dspark_ctx_kv_writer *w, const void *all_kv,
+                                           int64_t num_ctx, int32_t num_layers,
+                                           int32_t num_kv_heads, const void *k_norm_weight,
+                                           float eps, const int64_t *positions,
+                                           const void *cos_sin_cache, int64_t cos_sin_rows,
+                                           int32_t rotary_dim,
+                                           const int64_t *const *slot_mappings, void *stream) {
+    if (slot_mappings == nullptr && num_ctx > 0)
+        return fail(DSPARK_E_ARG, "slot_mappings is NULL");
+    return write_impl(w, all_kv, num_ctx, num_layers, num_kv_heads, k_norm_weight, eps, positions,
+                      cos_sin_cache, cos_sin_rows, rotary_dim, nullptr, slot_mappings, stream);
 }
 
 void dspark_ctx_kv_writer_destroy(dspark_ctx_kv_writer *w) { delete w; }

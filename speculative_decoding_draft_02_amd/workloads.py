@@ -42,7 +42,7 @@ class Workload:
     all_kv: np.ndarray         # uint16 bf16 bits [num_ctx, L, 2, nkv, 128]
     k_norm_weight: np.ndarray  # uint16 bf16 bits [L, 128]
     positions: np.ndarray      # int64 [num_ctx]
-    slot_mapping: np.ndarray   # int64 [num_ctx], < 0 = padding
+    slot_mapping: np.ndarray   # int64 [num_ctx] (shared) or [L, num_ctx] (per layer), < 0 = padding
     cos_sin: np.ndarray        # uint16 bf16 bits [rows, R] = [cos | sin]
     k_scales: np.ndarray       # float32 [L]
     v_scales: np.ndarray       # float32 [L]
@@ -61,7 +61,9 @@ class Workload:
 
     @property
     def valid_tokens(self) -> int:
-        return int(np.count_nonzero(self.slot_mapping >= 0))
+        """Tokens written (shared mapping), or token-layers written / L."""
+        return int(np.count_nonzero(self.slot_mapping >= 0)) // (
+            self.num_layers if self.slot_mapping.ndim == 2 else 1)
 
     def new_host_caches(self):
         return [np.full(self.cache_shape, self.sentinel, dtype=self.cache_np_dtype)
@@ -70,14 +72,22 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Bytes the write must move: all_kv rows of valid tokens read, cache
         rows written, the cos/sin row and position of each valid token, every
-        slot, and the norm weights."""
-        v = self.valid_tokens
+        slot, and the norm weights.  With per-layer mappings a (token, layer)
+        is valid on its own and each token reads its cos/sin row once."""
         L, nkv, R = self.num_layers, self.num_kv_heads, self.rotary_dim
         e = 1 if self.fp8 else 2
+        if self.slot_mapping.ndim == 2:
+            tl = int(np.count_nonzero(self.slot_mapping >= 0))
+            tok = int(np.count_nonzero((self.slot_mapping >= 0).any(axis=0)))
+            per_tl = 2 * nkv * HEAD_DIM * 2 + nkv * 2 * HEAD_DIM * e
+            return tl * per_tl + tok * (2 * R + 8) + 8 * L * self.num_ctx + L * HEAD_DIM * 2
+        v = self.valid_tokens
         per_tok = L * 2 * nkv * HEAD_DIM * 2 + L * nkv * 2 * HEAD_DIM * e + 2 * R + 8
         return v * per_tok + 8 * self.num_ctx + L * HEAD_DIM * 2
 
     def token_layers(self) -> int:
+        if self.slot_mapping.ndim == 2:
+            return int(np.count_nonzero(self.slot_mapping >= 0))
         return self.valid_tokens * self.num_layers
 
 
@@ -223,6 +233,22 @@ def make(index: int, variant: int = 0) -> Workload:
     return Workload(NAMES[index], N, L, nkv, R, bs, nb, fp8, eps,
                     np.ascontiguousarray(all_kv), np.ascontiguousarray(w),
                     positions, slots, cs, ks, vs)
+
+
+def per_layer_slots(wl: Workload, seed: int, pad_fraction: float = 0.05) -> Workload:
+    """The same inputs with one slot mapping per layer ([L, num_ctx]): every
+    layer places the tokens in its own random blocks (as when the draft's
+    layers belong to different KV-cache groups) and pads its own tokens."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    L, N, bs, nb = wl.num_layers, wl.num_ctx, wl.block_size, wl.num_blocks
+    base = wl.slot_mapping if wl.slot_mapping.ndim == 1 else wl.slot_mapping[0]
+    maps = np.empty((L, N), np.int64)
+    for l in range(L):
+        perm = rng.permutation(nb)
+        s = np.where(base >= 0, perm[np.maximum(base, 0) // bs] * bs + np.maximum(base, 0) % bs, -1)
+        maps[l] = _pad(rng, s.astype(np.int64), int(round(pad_fraction * N)))
+    return dataclasses.replace(wl, slot_mapping=maps)
 
 
 def custom(num_ctx, num_layers, num_kv_heads, rotary_dim, block_size, num_blocks,

@@ -26,6 +26,23 @@ def rotary_dims_supported(rotary_dim: int, head_dim: int) -> bool:
     return bool(_lib.dspark_rotary_dims_supported(int(rotary_dim), int(head_dim)))
 
 
+def _split_slot_mapping(slot_mapping, num_layers):
+    """(shared tensor, None) or (None, list of per-layer tensors)."""
+    if isinstance(slot_mapping, torch.Tensor):
+        if slot_mapping.dim() == 1:
+            return slot_mapping, None
+        if slot_mapping.dim() == 2 and slot_mapping.shape[0] == num_layers:
+            return None, [slot_mapping[l] for l in range(num_layers)]
+        raise ValueError("slot_mapping must be [num_ctx] or [num_layers, num_ctx]")
+    maps = list(slot_mapping)
+    if len(maps) != num_layers or any(m is None for m in maps):
+        raise ValueError(f"expected {num_layers} per-layer slot mappings, none of them None")
+    first = maps[0]
+    if all(m.data_ptr() == first.data_ptr() for m in maps):
+        return first, None
+    return None, maps
+
+
 @dataclass
 class AttnLayer:
     """The attributes of a draft attention layer that the writer reads."""
@@ -147,34 +164,51 @@ class DSparkContextKVWriter:
 
     def __call__(self, all_kv: torch.Tensor, k_norm_weight: torch.Tensor, eps: float,
                  positions: torch.Tensor, cos_sin_cache: torch.Tensor, rotary_dim: int,
-                 slot_mapping: torch.Tensor) -> None:
+                 slot_mapping) -> None:
+        """slot_mapping: one int64 [num_ctx] tensor shared by every layer, or
+        a list of L such tensors (one per layer, as the model passes when its
+        layers span several KV-cache groups), or an int64 [L, num_ctx]
+        tensor.  A list whose entries are all the same tensor is the shared
+        case (the rule of _shared_slot_mapping)."""
         num_ctx, L, two, nkv, hd = all_kv.shape
         assert self._num_layers == L and self._num_kv_heads == nkv
         assert two == 2 and hd == HEAD_DIM
         if num_ctx == 0:
             return
         dev = self._layers[0].kv_cache.device
+        shared, per_layer = _split_slot_mapping(slot_mapping, L)
         for name, t, dt in (("all_kv", all_kv, torch.bfloat16),
                             ("k_norm_weight", k_norm_weight, torch.bfloat16),
                             ("positions", positions, torch.int64),
-                            ("cos_sin_cache", cos_sin_cache, torch.bfloat16),
-                            ("slot_mapping", slot_mapping, torch.int64)):
+                            ("cos_sin_cache", cos_sin_cache, torch.bfloat16)):
             if t.dtype != dt or t.device != dev or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+        for t in ([shared] if shared is not None else per_layer):
+            if t.dtype != torch.int64 or t.device != dev or not t.is_contiguous() \
+                    or t.shape != (num_ctx,):
+                raise ValueError(f"slot mappings must be contiguous int64 ({num_ctx},) "
+                                 f"tensors on {dev}")
         if tuple(k_norm_weight.shape) != (L, HEAD_DIM):
             raise ValueError(f"k_norm_weight has shape {tuple(k_norm_weight.shape)}, "
                              f"expected {(L, HEAD_DIM)}")
-        if positions.shape != (num_ctx,) or slot_mapping.shape != (num_ctx,):
-            raise ValueError("positions and slot_mapping must have shape (num_ctx,)")
+        if positions.shape != (num_ctx,):
+            raise ValueError("positions must have shape (num_ctx,)")
         if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != rotary_dim:
             raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}, "
                              f"expected (rows, {rotary_dim})")
         self._ensure_tables()
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = _lib.dspark_ctx_kv_writer_write(
-            self._handle, all_kv.data_ptr(), num_ctx, L, nkv, k_norm_weight.data_ptr(),
-            float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
-            int(rotary_dim), slot_mapping.data_ptr(), stream)
+        if shared is not None:
+            st = _lib.dspark_ctx_kv_writer_write(
+                self._handle, all_kv.data_ptr(), num_ctx, L, nkv, k_norm_weight.data_ptr(),
+                float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
+                cos_sin_cache.shape[0], int(rotary_dim), shared.data_ptr(), stream)
+        else:
+            st = _lib.dspark_ctx_kv_writer_write_layer_slots(
+                self._handle, all_kv.data_ptr(), num_ctx, L, nkv, k_norm_weight.data_ptr(),
+                float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
+                cos_sin_cache.shape[0], int(rotary_dim), [t.data_ptr() for t in per_layer],
+                stream)
         if st != _lib.OK:
             raise RuntimeError("DSpark context-KV write failed: " + _lib.dspark_ctx_kv_last_error())
 

@@ -58,9 +58,9 @@ def compact_blocks(wl: W.Workload) -> W.Workload:
     s = wl.slot_mapping
     blocks = np.unique(s[s >= 0] // wl.block_size)
     remap = {int(b): i for i, b in enumerate(blocks)}
-    new = np.array([remap[int(x) // wl.block_size] * wl.block_size + int(x) % wl.block_size
-                    if x >= 0 else -1 for x in s], np.int64)
-    return dataclasses.replace(wl, slot_mapping=new, num_blocks=max(len(blocks), 1))
+    flat = np.array([remap[int(x) // wl.block_size] * wl.block_size + int(x) % wl.block_size
+                     if x >= 0 else -1 for x in s.reshape(-1)], np.int64)
+    return dataclasses.replace(wl, slot_mapping=flat.reshape(s.shape), num_blocks=max(len(blocks), 1))
 
 
 # ------------------------------------------------------------------------
@@ -94,11 +94,13 @@ def torch_unfused(wl: W.Workload):
     o2 = (x2 * cos + x1 * sin).to(torch.bfloat16)
     k = torch.cat([o1, o2, k[..., R:]], dim=-1)
     caches = wl.new_host_caches()
-    slots = torch.from_numpy(wl.slot_mapping)
-    valid = torch.nonzero(slots >= 0).flatten()
-    s = slots[valid]
-    blk, off = s // wl.block_size, s % wl.block_size
+    all_slots = torch.from_numpy(wl.slot_mapping)
     for l in range(L):
+        # per-layer reshape_and_cache_flash: layer l's own mapping if given
+        slots = all_slots[l] if all_slots.dim() == 2 else all_slots
+        valid = torch.nonzero(slots >= 0).flatten()
+        s = slots[valid]
+        blk, off = s // wl.block_size, s % wl.block_size
         kk, vv = k[l, valid], all_v[l, valid]                      # [V,H,D]
         if wl.fp8:
             kq = (kk.float() / float(wl.k_scales[l])).clamp(-448.0, 448.0)

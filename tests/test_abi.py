@@ -190,3 +190,42 @@ def test_python_writer_validate_reasons_on_cpu_tensors():
     assert V([AttnLayer(cache, sc, sc)]) == "_k_scale is not a CUDA fp32 tensor"
     with pytest.raises(ValueError, match="unsupported DSpark context-KV layout: no layers"):
         DSparkContextKVWriter([])
+
+
+def test_layer_slots_entry_argument_checks(lib):
+    st, w = _lib.dspark_ctx_kv_writer_create(*_layout(L=3))
+    assert st == _lib.OK
+    fake = BASE + 0x100000
+
+    def write(maps, num_ctx=16, num_layers=3):
+        return _lib.dspark_ctx_kv_writer_write_layer_slots(
+            w, fake, num_ctx, num_layers, 8, fake, 1e-6, fake, fake, 4096, 64, maps, None)
+
+    assert write([fake, fake, 0]) == _lib.E_ARG
+    assert "slot mapping of layer 2 is NULL" in _lib.dspark_ctx_kv_last_error()
+    assert write([fake, fake + 4, fake]) == _lib.E_ARG
+    assert "not 8-byte aligned" in _lib.dspark_ctx_kv_last_error()
+    assert write([fake] * 3, num_layers=2) == _lib.E_ARG
+    assert write([fake] * 3, num_ctx=0) == _lib.OK       # no-op, no launch
+    L = _lib.load()
+    assert L.dspark_ctx_kv_writer_write_layer_slots(w, fake, 4, 3, 8, fake, 1e-6, fake, fake,
+                                                    4096, 64, None, None) == _lib.E_ARG
+    _lib.dspark_ctx_kv_writer_destroy(w)
+
+
+def test_python_writer_splits_slot_mappings():
+    import torch
+    from speculative_decoding_draft_02_amd.writer import _split_slot_mapping
+    a = torch.arange(6)
+    b = torch.arange(6)
+    assert _split_slot_mapping(a, 3)[0] is a
+    shared, per = _split_slot_mapping([a, a, a], 3)
+    assert shared is a and per is None
+    shared, per = _split_slot_mapping([a, b, a], 3)
+    assert shared is None and len(per) == 3
+    shared, per = _split_slot_mapping(torch.zeros(3, 6, dtype=torch.int64), 3)
+    assert shared is None and len(per) == 3
+    with pytest.raises(ValueError):
+        _split_slot_mapping([a, None, a], 3)
+    with pytest.raises(ValueError):
+        _split_slot_mapping([a, a], 3)

@@ -211,3 +211,58 @@ def test_error_paths():
     with pytest.raises(ValueError, match="16-element aligned"):
         DSparkContextKVWriter(mis)
     assert DSparkContextKVWriter.supported(layers)
+
+
+# ------------------------------------------------- per-layer slot mappings --
+
+LAYER_SLOT_CASES = [
+    # N, L, nkv, R, bs, blocks, fp8
+    (300, 5, 8, 64, 64, 32, False),
+    (300, 5, 8, 32, 16, 64, True),
+    (129, 3, 2, 16, 4, 80, False),
+    (65, 9, 3, 64, 8, 32, True),       # L > 8: chunked pass
+    (257, 4, 5, 32, 128, 8, False),
+]
+
+
+@pytest.mark.parametrize("shape", LAYER_SLOT_CASES, ids=lambda s: "N%d-L%d-H%d-R%d-bs%d-%s" % (
+    s[0], s[1], s[2], s[3], s[4], "fp8" if s[6] else "bf16"))
+def test_per_layer_slot_parity(oracle_lib, shape):
+    N, L, nkv, R, bs, nb, fp8 = shape
+    wl = W.custom(N, L, nkv, R, bs, nb, fp8, seed=7 * N + L, pad_fraction=0.05,
+                  kv_std=4.0 if fp8 else 1.0)
+    wl = W.per_layer_slots(wl, seed=N + 3, pad_fraction=0.15)
+    _check(oracle_lib, wl, label="layer-slots")
+
+
+def test_per_layer_slot_list_forms():
+    """A list of the same tensor takes the shared path; a list of distinct
+    tensors and an [L, N] tensor give the same caches."""
+    wl = W.per_layer_slots(W.custom(100, 3, 4, 32, 16, 32, False, seed=3, pad_fraction=0.1),
+                           seed=4, pad_fraction=0.1)
+    outs = []
+    for form in ("tensor", "list"):
+        layers = make_layers(wl)
+        writer = DSparkContextKVWriter(layers)
+        inp = DeviceInputs(wl)
+        slots = inp.slots if form == "tensor" else [inp.slots[l].clone() for l in range(3)]
+        writer(inp.all_kv, inp.w, wl.eps, inp.positions, inp.cos_sin, wl.rotary_dim, slots)
+        torch.cuda.synchronize()
+        outs.append([cache_codes(a.kv_cache) for a in layers])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    # identical per-layer mappings equal the shared write
+    wl2 = W.custom(100, 3, 4, 32, 16, 32, False, seed=5, pad_fraction=0.1)
+    res = []
+    for form in ("shared", "same-list", "stacked"):
+        layers = make_layers(wl2)
+        writer = DSparkContextKVWriter(layers)
+        inp = DeviceInputs(wl2)
+        slots = {"shared": inp.slots, "same-list": [inp.slots] * 3,
+                 "stacked": inp.slots.unsqueeze(0).repeat(3, 1).contiguous()}[form]
+        writer(inp.all_kv, inp.w, wl2.eps, inp.positions, inp.cos_sin, wl2.rotary_dim, slots)
+        torch.cuda.synchronize()
+        res.append([cache_codes(a.kv_cache) for a in layers])
+    for other in res[1:]:
+        for a, b in zip(res[0], other):
+            assert np.array_equal(a, b)

@@ -319,3 +319,36 @@ def test_acceptance_rule_catches_planted_mistakes(oracle_lib):
         else:
             bad[0][5, 0, 3, 7] = 0
         assert C.compare(bad, res, wl.slot_mapping, False, wl.sentinel).failures > 0, mutate
+
+
+# ------------------------------------------------- per-layer slot mappings --
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_oracle_per_layer_slots_vs_torch_unfused(oracle_lib, fp8):
+    """One mapping per layer: each layer's rows land at its own slots and a
+    slot < 0 skips that layer only; the unfused chain with per-layer
+    reshape_and_cache agrees under the acceptance rule."""
+    wl = W.custom(40, 3, 2, 32, 4, 40, fp8, seed=31, pad_fraction=0.1, kv_std=4.0 if fp8 else 1.0)
+    wl = W.per_layer_slots(wl, seed=32, pad_fraction=0.2)
+    assert wl.slot_mapping.shape == (3, 40)
+    ref = torch_unfused(wl)
+    caches = wl.new_host_caches()
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  32, wl.slot_mapping, caches, fp8, wl.k_scales, wl.v_scales)
+    rep = C.compare(ref, res, wl.slot_mapping, fp8, wl.sentinel)
+    assert rep.failures == 0, rep.totals()
+    # layers differ in what they wrote
+    written = [int(np.count_nonzero(np.any(c.reshape(-1, 256) != wl.sentinel, axis=1))) for c in caches]
+    assert written == [2 * int(np.count_nonzero(wl.slot_mapping[l] >= 0)) for l in range(3)]
+
+
+def test_oracle_identical_per_layer_slots_equal_shared(oracle_lib):
+    wl = W.custom(30, 4, 2, 64, 8, 8, False, seed=33, pad_fraction=0.2)
+    shared = wl.new_host_caches()
+    oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin, 64,
+                            wl.slot_mapping, shared, False)
+    per = wl.new_host_caches()
+    oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin, 64,
+                            np.stack([wl.slot_mapping] * 4), per, False)
+    for a, b in zip(shared, per):
+        assert np.array_equal(a, b)
