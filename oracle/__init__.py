@@ -1,4 +1,5 @@
-"""Exact-value CPU oracle for the DSpark fused context-KV write.
+"""Exact-value CPU oracle for the DSpark fused context-KV write and the
+draft block's fused QK-norm / RoPE / KV insert.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The product
@@ -74,6 +75,16 @@ def lib():
             P, P, P, P, i64,             # alt_layer, alt_index, alt_count, alt_codes, cap
             i64, i64]                    # t_begin, t_end
         L.dspark_oracle_ctx_kv_write.restype = i64
+        L.dspark_oracle_qknorm_rope_kv_insert.argtypes = [
+            P, i64, i32, i32,            # qkv, num_tokens, num_heads, nkv
+            P, P, ctypes.c_float,        # q_norm_weight, k_norm_weight, eps
+            P, P, i64, i32,              # positions, cos_sin, cs_rows, R
+            P, P, i64, i32,              # slot_mapping, cache, num_blocks, block_size
+            i32, ctypes.c_float, ctypes.c_float,   # fp8, k_scale, v_scale
+            P, ctypes.c_float,           # q_fp8, q_scale
+            ctypes.c_double,             # near_delta
+            P, P, P, P, i64]             # alt_tag, alt_index, alt_count, alt_codes, cap
+        L.dspark_oracle_qknorm_rope_kv_insert.restype = i64
         _lib = L
     return _lib
 
@@ -173,4 +184,67 @@ def ctx_kv_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim,
             raise ValueError("oracle precondition failed (code %d)" % n)
         if n <= cap:
             return OracleResult(caches, a_layer[:n], a_index[:n], a_count[:n], a_codes[:n])
+        cap = int(n)
+
+
+# ------------------------------------------- the draft-block insert ----
+
+@dataclass
+class InsertResult:
+    qkv: np.ndarray            # uint16 [T, (H + 2 nkv) * 128], q and k heads normed and rotated
+    cache: np.ndarray | None   # the cache after the insert (the array passed in), or None
+    q_fp8: np.ndarray | None   # uint8 [T, H * 128] or None
+    alt_tag: np.ndarray        # int64 [n]: 0 qkv, 1 cache, 2 q_fp8
+    alt_index: np.ndarray      # int64 [n], element index into that flat output
+    alt_count: np.ndarray      # int32 [n]
+    alt_codes: np.ndarray      # uint16 [n, 4]
+
+
+def qknorm_rope_kv_insert(qkv, num_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
+                          positions, cos_sin, rotary_dim, slot_mapping=None, cache=None,
+                          fp8=False, k_scale=1.0, v_scale=1.0, want_q_fp8=False, q_scale=1.0,
+                          near_delta: float = NEAR_DELTA) -> InsertResult:
+    """Run the draft-block oracle on host arrays.  ``qkv`` (uint16
+    [T, (H + 2 nkv) * 128]) is read only: the updated copy is returned.
+    ``cache`` ([num_blocks, nkv, bs, 256], uint16 for bf16 or uint8 for fp8)
+    is written in place when slot_mapping is given."""
+    src = np.ascontiguousarray(qkv, dtype=np.uint16)
+    T = src.shape[0]
+    H, nkv = int(num_heads), int(num_kv_heads)
+    assert src.shape == (T, (H + 2 * nkv) * HEAD_DIM)
+    qw = np.ascontiguousarray(q_norm_weight, dtype=np.uint16).reshape(HEAD_DIM)
+    kw = np.ascontiguousarray(k_norm_weight, dtype=np.uint16).reshape(HEAD_DIM)
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    assert pos.shape == (T,)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.uint16)
+    assert cs.ndim == 2 and cs.shape[1] == rotary_dim
+    slots_ptr, cache_ptr, nb, bs = None, None, 0, 0
+    if slot_mapping is not None:
+        slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        assert slots.shape == (T,)
+        assert cache is not None and cache.flags.c_contiguous and cache.ndim == 4
+        assert cache.dtype == (np.uint8 if fp8 else np.uint16)
+        nb, c_nkv, bs, width = cache.shape
+        assert c_nkv == nkv and width == 2 * HEAD_DIM
+        slots_ptr, cache_ptr = slots.ctypes.data, cache.ctypes.data
+    cap = max(1024, T * (H + nkv) * 2)
+    while True:
+        out = src.copy()
+        qf = np.zeros((T, H * HEAD_DIM), np.uint8) if want_q_fp8 else None
+        a_tag = np.zeros(cap, np.int64)
+        a_index = np.zeros(cap, np.int64)
+        a_count = np.zeros(cap, np.int32)
+        a_codes = np.zeros((cap, MAX_CAND), np.uint16)
+        n = lib().dspark_oracle_qknorm_rope_kv_insert(
+            out.ctypes.data, T, H, nkv, qw.ctypes.data, kw.ctypes.data, float(eps),
+            pos.ctypes.data, cs.ctypes.data, cs.shape[0], rotary_dim,
+            slots_ptr, cache_ptr, nb, bs, 1 if fp8 else 0, float(k_scale), float(v_scale),
+            qf.ctypes.data if qf is not None else None, float(q_scale), float(near_delta),
+            a_tag.ctypes.data, a_index.ctypes.data, a_count.ctypes.data, a_codes.ctypes.data,
+            cap)
+        if n < 0:
+            raise ValueError("oracle precondition failed (code %d)" % n)
+        if n <= cap:
+            return InsertResult(out, cache if slot_mapping is not None else None, qf,
+                                a_tag[:n], a_index[:n], a_count[:n], a_codes[:n])
         cap = int(n)

@@ -166,3 +166,104 @@ def compare(device_caches, oracle_result, slot_mapping, fp8: bool, sentinel: int
             stats.max_dist = maxd
         layers.append(rep)
     return Report(layers=layers, fp8=fp8)
+
+
+# ------------------------------------------------ the draft-block insert ----
+#
+# The same rule for dspark_qknorm_rope_kv_insert's three outputs:
+#   * qkv, q and k heads: ordinal bf16 distance <= 1 from the oracle's code or
+#     an alternate; v heads: bit-exact (they are not touched);
+#   * the cache: as above (K bf16 within 1 / alternates, V bf16 bit-exact,
+#     fp8 within 1 e4m3 step), and every row no slot names keeps the sentinel;
+#   * q_fp8: ordinal e4m3 distance <= 1 from the oracle's code or an alternate.
+
+def _grade(dev: np.ndarray, ora: np.ndarray, flat_index: np.ndarray, alt_map: dict,
+           ordf, bit_exact: bool) -> PartStats:
+    s = PartStats(n=int(dev.size))
+    if dev.size == 0:
+        return s
+    same = dev == ora
+    s.exact = int(np.count_nonzero(same))
+    if bit_exact:
+        s.fail = int(dev.size - s.exact)
+        if s.fail:
+            s.max_dist = int(np.abs(ordf(dev[~same]) - ordf(ora[~same])).max())
+        return s
+    d = np.abs(ordf(dev) - ordf(ora))
+    s.within1 = int(np.count_nonzero((d <= 1) & ~same))
+    s.max_dist = int(d.max())
+    for pos in np.flatnonzero(d.reshape(-1) > 1):
+        cands = alt_map.get(int(flat_index.reshape(-1)[pos]))
+        got = dev.reshape(-1)[pos]
+        if cands is not None and np.abs(ordf(np.asarray(cands)) - ordf(np.asarray([got]))).min() <= 1:
+            s.by_alternate += 1
+        else:
+            s.fail += 1
+    return s
+
+
+@dataclass
+class InsertReport:
+    parts: dict
+    untouched_bad: int
+
+    @property
+    def failures(self) -> int:
+        return sum(p.fail for p in self.parts.values()) + self.untouched_bad
+
+    def totals(self) -> dict:
+        out = {k: v.as_dict() for k, v in self.parts.items()}
+        out["untouched_bad"] = self.untouched_bad
+        out["failures"] = self.failures
+        return out
+
+
+def compare_insert(dev_qkv, dev_cache, dev_q_fp8, oracle_result, num_heads: int,
+                   num_kv_heads: int, slot_mapping, fp8: bool, sentinel: int) -> InsertReport:
+    """Grade the device outputs of the draft-block insert against the oracle's
+    (an oracle.InsertResult); dev_cache / dev_q_fp8 may be None when the call
+    had no insert / no q fp8 output."""
+    H, nkv = num_heads, num_kv_heads
+    r = oracle_result
+
+    def alt_map(tag):
+        sel = r.alt_tag == tag
+        idx, cnt, codes = r.alt_index[sel], r.alt_count[sel], r.alt_codes[sel]
+        return {int(i): codes[k, :cnt[k]] for k, i in enumerate(idx)}
+
+    parts = {}
+    dq = np.asarray(dev_qkv)
+    oq = r.qkv
+    assert dq.shape == oq.shape and dq.dtype == oq.dtype
+    T, width = oq.shape
+    flat = np.arange(T * width, dtype=np.int64).reshape(T, width)
+    m = alt_map(0)
+    qe, ke = H * 128, (H + nkv) * 128
+    parts["q"] = _grade(dq[:, :qe], oq[:, :qe], flat[:, :qe], m, ordinal_bf16, False)
+    parts["k"] = _grade(dq[:, qe:ke], oq[:, qe:ke], flat[:, qe:ke], m, ordinal_bf16, False)
+    parts["v"] = _grade(dq[:, ke:], oq[:, ke:], flat[:, ke:], m, ordinal_bf16, True)
+
+    untouched = 0
+    if r.cache is not None:
+        dc = np.asarray(dev_cache)
+        oc = r.cache
+        assert dc.shape == oc.shape and dc.dtype == oc.dtype
+        bs = oc.shape[2]
+        rows = written_rows(slot_mapping, nkv, bs)
+        d2 = dc.reshape(-1, 256)
+        o2 = oc.reshape(-1, 256)
+        mask = np.ones(d2.shape[0], dtype=bool)
+        mask[rows] = False
+        untouched = int(np.count_nonzero(d2[mask] != sentinel))
+        cflat = rows[:, None] * 256 + np.arange(256, dtype=np.int64)[None, :]
+        m = alt_map(1)
+        ordf = ordinal_e4m3 if fp8 else ordinal_bf16
+        parts["cache_k"] = _grade(d2[rows, :128], o2[rows, :128], cflat[:, :128], m, ordf, False)
+        parts["cache_v"] = _grade(d2[rows, 128:], o2[rows, 128:], cflat[:, 128:], m, ordf,
+                                  not fp8)
+    if r.q_fp8 is not None:
+        df = np.asarray(dev_q_fp8)
+        assert df.shape == r.q_fp8.shape
+        qflat = np.arange(df.size, dtype=np.int64).reshape(df.shape)
+        parts["q_fp8"] = _grade(df, r.q_fp8, qflat, alt_map(2), ordinal_e4m3, False)
+    return InsertReport(parts=parts, untouched_bad=untouched)

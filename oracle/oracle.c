@@ -188,6 +188,89 @@ static int add_candidate(uint16_t *set, int n, uint16_t c)
     return n + 1;
 }
 
+/* Gemma RMSNorm of one 128-value bf16 row followed by partial NeoX RoPE, as
+ * the unfused chain computes it: the norm x * rsqrt(mean(x^2) + eps) * (1 + w)
+ * evaluated exactly (fp64) and rounded once to bf16, then the rotation of the
+ * pairs (i, i + R/2) of that bf16 output by the table row [cos | sin], each
+ * result rounded once to bf16; dims R..127 keep the norm output.
+ * kcode receives the codes; kcand[i][0..ncand[i]) every code that a near tie
+ * of the norm output can lead to (kcand[i][0] == kcode[i]). */
+static void norm_rope_row(const uint16_t *row, const uint16_t *w, float eps,
+                          const uint16_t *cs_row, int R, double near_delta,
+                          uint16_t kcode[HEAD_DIM], uint16_t kcand[HEAD_DIM][MAX_CAND],
+                          int ncand_k[HEAD_DIM])
+{
+    double x[HEAD_DIM];
+    uint16_t ycode[HEAD_DIM];
+    uint16_t ycand[HEAD_DIM][2];
+    int ncand_y[HEAD_DIM];
+
+    double ss = 0.0;
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        x[i] = dspark_oracle_bf16_decode(row[i]);
+        ss += x[i] * x[i];
+    }
+    double r = 1.0 / sqrt(ss / HEAD_DIM + (double)eps);
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        double wi = dspark_oracle_bf16_decode(w[i]);
+        double z = x[i] * r * (1.0 + wi);
+        int near = 0;
+        uint16_t other = 0;
+        ycode[i] = dspark_oracle_bf16_round(z, near_delta, &near, &other);
+        ycand[i][0] = ycode[i];
+        ncand_y[i] = 1;
+        if (near) {
+            ycand[i][1] = other;
+            ncand_y[i] = 2;
+        }
+    }
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        kcode[i] = ycode[i];
+        ncand_k[i] = 0;
+    }
+    for (int i = 0; i < R / 2; ++i) {
+        int j = i + R / 2;
+        double c = dspark_oracle_bf16_decode(cs_row[i]);
+        double s = dspark_oracle_bf16_decode(cs_row[R / 2 + i]);
+        double a0 = dspark_oracle_bf16_decode(ycode[i]);
+        double b0 = dspark_oracle_bf16_decode(ycode[j]);
+        kcode[i] = dspark_oracle_bf16_round(a0 * c - b0 * s, 0.0, NULL, NULL);
+        kcode[j] = dspark_oracle_bf16_round(b0 * c + a0 * s, 0.0, NULL, NULL);
+        for (int ia = 0; ia < ncand_y[i]; ++ia) {
+            for (int ib = 0; ib < ncand_y[j]; ++ib) {
+                double a = dspark_oracle_bf16_decode(ycand[i][ia]);
+                double b = dspark_oracle_bf16_decode(ycand[j][ib]);
+                ncand_k[i] = add_candidate(kcand[i], ncand_k[i],
+                    dspark_oracle_bf16_round(a * c - b * s, 0.0, NULL, NULL));
+                ncand_k[j] = add_candidate(kcand[j], ncand_k[j],
+                    dspark_oracle_bf16_round(b * c + a * s, 0.0, NULL, NULL));
+            }
+        }
+    }
+    for (int i = R; i < HEAD_DIM; ++i) {
+        ncand_k[i] = 0;
+        for (int ia = 0; ia < ncand_y[i]; ++ia)
+            ncand_k[i] = add_candidate(kcand[i], ncand_k[i], ycand[i][ia]);
+    }
+}
+
+/* Record an element with more than one correct code. */
+static void record_alternates(int64_t *n_alt, int64_t capacity, int64_t tag, int64_t index,
+                              const uint16_t *codes, int nc, int64_t *alt_tag,
+                              int64_t *alt_index, int32_t *alt_count, uint16_t *alt_codes)
+{
+    if (nc <= 1)
+        return;
+    if (*n_alt < capacity) {
+        alt_tag[*n_alt] = tag;
+        alt_index[*n_alt] = index;
+        alt_count[*n_alt] = nc;
+        for (int q = 0; q < MAX_CAND; ++q)
+            alt_codes[*n_alt * MAX_CAND + q] = q < nc ? codes[q] : 0;
+    }
+    ++*n_alt;
+}
+
 /*
  * The whole write, on host buffers.
  *
@@ -238,10 +321,6 @@ int64_t dspark_oracle_ctx_kv_write(
         return -5;
 
     int64_t n_alt = 0;
-    double x[HEAD_DIM];
-    uint16_t ycode[HEAD_DIM];
-    uint16_t ycand[HEAD_DIM][2];
-    int ncand_y[HEAD_DIM];
     uint16_t kcand[HEAD_DIM][MAX_CAND];
     int ncand_k[HEAD_DIM];
     uint16_t kcode[HEAD_DIM];
@@ -266,56 +345,8 @@ int64_t dspark_oracle_ctx_kv_write(
                 const uint16_t *vrow =
                     all_kv + (((t * num_layers + l) * 2 + 1) * nkv + h) * HEAD_DIM;
 
-                /* Gemma RMSNorm: x * rsqrt(mean(x^2) + eps) * (1 + w) */
-                double ss = 0.0;
-                for (int i = 0; i < HEAD_DIM; ++i) {
-                    x[i] = dspark_oracle_bf16_decode(krow[i]);
-                    ss += x[i] * x[i];
-                }
-                double r = 1.0 / sqrt(ss / HEAD_DIM + (double)eps);
-                for (int i = 0; i < HEAD_DIM; ++i) {
-                    double w = dspark_oracle_bf16_decode(k_norm_weight[l * HEAD_DIM + i]);
-                    double z = x[i] * r * (1.0 + w);
-                    int near = 0;
-                    uint16_t other = 0;
-                    ycode[i] = dspark_oracle_bf16_round(z, near_delta, &near, &other);
-                    ycand[i][0] = ycode[i];
-                    ncand_y[i] = 1;
-                    if (near) {
-                        ycand[i][1] = other;
-                        ncand_y[i] = 2;
-                    }
-                }
-
-                /* partial NeoX RoPE on the bf16 norm output */
-                for (int i = 0; i < HEAD_DIM; ++i) {
-                    kcode[i] = ycode[i];
-                    ncand_k[i] = 0;
-                }
-                for (int i = 0; i < R / 2; ++i) {
-                    int j = i + R / 2;
-                    double c = dspark_oracle_bf16_decode(cs_row[i]);
-                    double s = dspark_oracle_bf16_decode(cs_row[R / 2 + i]);
-                    double a0 = dspark_oracle_bf16_decode(ycode[i]);
-                    double b0 = dspark_oracle_bf16_decode(ycode[j]);
-                    kcode[i] = dspark_oracle_bf16_round(a0 * c - b0 * s, 0.0, NULL, NULL);
-                    kcode[j] = dspark_oracle_bf16_round(b0 * c + a0 * s, 0.0, NULL, NULL);
-                    for (int ia = 0; ia < ncand_y[i]; ++ia) {
-                        for (int ib = 0; ib < ncand_y[j]; ++ib) {
-                            double a = dspark_oracle_bf16_decode(ycand[i][ia]);
-                            double b = dspark_oracle_bf16_decode(ycand[j][ib]);
-                            ncand_k[i] = add_candidate(kcand[i], ncand_k[i],
-                                dspark_oracle_bf16_round(a * c - b * s, 0.0, NULL, NULL));
-                            ncand_k[j] = add_candidate(kcand[j], ncand_k[j],
-                                dspark_oracle_bf16_round(b * c + a * s, 0.0, NULL, NULL));
-                        }
-                    }
-                }
-                for (int i = R; i < HEAD_DIM; ++i) {
-                    ncand_k[i] = 0;
-                    for (int ia = 0; ia < ncand_y[i]; ++ia)
-                        ncand_k[i] = add_candidate(kcand[i], ncand_k[i], ycand[i][ia]);
-                }
+                norm_rope_row(krow, k_norm_weight + l * HEAD_DIM, eps, cs_row, R, near_delta,
+                              kcode, kcand, ncand_k);
 
                 /* store into layer l's cache at [blk, h, off, :] */
                 int64_t row = ((blk * nkv + h) * block_size + off) * (2 * HEAD_DIM);
@@ -336,16 +367,135 @@ int64_t dspark_oracle_ctx_kv_write(
                         for (int q = 0; q < ncand_k[i]; ++q)
                             nc = add_candidate(codes, nc, kcand[i][q]);
                     }
-                    if (nc > 1) {
-                        if (n_alt < alt_capacity) {
-                            alt_layer[n_alt] = l;
-                            alt_index[n_alt] = row + i;
-                            alt_count[n_alt] = nc;
-                            for (int q = 0; q < MAX_CAND; ++q)
-                                alt_codes[n_alt * MAX_CAND + q] = q < nc ? codes[q] : 0;
-                        }
-                        ++n_alt;
+                    record_alternates(&n_alt, alt_capacity, l, row + i, codes, nc,
+                                      alt_layer, alt_index, alt_count, alt_codes);
+                }
+            }
+        }
+    }
+    return n_alt;
+}
+
+/* ------------------------------------------- draft-block QK norm + RoPE --- */
+
+/*
+ * The fused QK-norm / RoPE on the draft block's qkv, also storing the draft
+ * tokens' K/V (vLLM API page "vllm.models.minimax_m3.common.dspark",
+ * dspark_qknorm_rope_kv_insert; the per-head Gemma RMSNorm on Q and K before
+ * partial RoPE is the NeMo page's description of the same draft attention).
+ *
+ * qkv            bf16 bits [num_tokens, (H + 2 nkv) * 128]: H q heads, then
+ *                nkv k heads, then nkv v heads; rewritten in place: every q
+ *                and k head is replaced by its normed and rotated bf16 value,
+ *                v heads are left as they are
+ * q_norm_weight, k_norm_weight  bf16 bits [128], shared by the heads
+ * positions      int64 [num_tokens]; cos_sin bf16 bits [cs_rows, R]
+ * slot_mapping   NULL (no insert) or int64 [num_tokens], < 0 = not stored
+ * cache          NULL or [num_blocks, nkv, bs, 256] of uint16 (bf16) or uint8
+ *                (fp8): K at [..., :128], V at [..., 128:]
+ * k_scale, v_scale  fp32 scales of an fp8 cache
+ * q_fp8          NULL or uint8 [num_tokens, H * 128]: e4m3 of q / q_scale
+ * alt_tag        which output an alternate belongs to: 0 qkv, 1 cache, 2 q_fp8
+ *
+ * Returns the number of alternates, or -1 rotary dim, -2 block size,
+ * -3 position, -4 slot, -5 sizes.
+ */
+int64_t dspark_oracle_qknorm_rope_kv_insert(
+    uint16_t *qkv, int64_t num_tokens, int32_t num_heads, int32_t nkv,
+    const uint16_t *q_norm_weight, const uint16_t *k_norm_weight, float eps,
+    const int64_t *positions, const uint16_t *cos_sin, int64_t cs_rows, int32_t rotary_dim,
+    const int64_t *slot_mapping, void *cache, int64_t num_blocks, int32_t block_size,
+    int32_t fp8, float k_scale, float v_scale,
+    uint8_t *q_fp8, float q_scale,
+    double near_delta,
+    int64_t *alt_tag, int64_t *alt_index, int32_t *alt_count, uint16_t *alt_codes,
+    int64_t alt_capacity)
+{
+    const int R = rotary_dim;
+    if (R != 16 && R != 32 && R != 64)
+        return -1;
+    if (slot_mapping != NULL && (block_size <= 0 || (block_size & (block_size - 1))))
+        return -2;
+    if (num_tokens < 0 || num_heads <= 0 || nkv <= 0)
+        return -5;
+    const int64_t row_len = (int64_t)(num_heads + 2 * nkv) * HEAD_DIM;
+    int64_t n_alt = 0;
+    uint16_t kcand[HEAD_DIM][MAX_CAND];
+    int ncand_k[HEAD_DIM];
+    uint16_t kcode[HEAD_DIM];
+    uint16_t src[HEAD_DIM];
+
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t p = positions[t];
+        if (p < 0 || p >= cs_rows)
+            return -3;
+        const uint16_t *cs_row = cos_sin + p * R;
+        int64_t slot = -1;
+        if (slot_mapping != NULL && cache != NULL) {
+            slot = slot_mapping[t];
+            if (slot >= num_blocks * (int64_t)block_size)
+                return -4;
+        }
+        uint16_t *tok = qkv + t * row_len;
+
+        /* q heads, then k heads: norm + RoPE, written back in place */
+        for (int hh = 0; hh < num_heads + nkv; ++hh) {
+            const int is_k = hh >= num_heads;
+            uint16_t *row = tok + (int64_t)hh * HEAD_DIM;
+            memcpy(src, row, sizeof src);
+            norm_rope_row(src, is_k ? k_norm_weight : q_norm_weight, eps, cs_row, R,
+                          near_delta, kcode, kcand, ncand_k);
+            for (int i = 0; i < HEAD_DIM; ++i) {
+                row[i] = kcode[i];
+                record_alternates(&n_alt, alt_capacity, 0, t * row_len + hh * HEAD_DIM + i,
+                                  kcand[i], ncand_k[i], alt_tag, alt_index, alt_count,
+                                  alt_codes);
+            }
+            if (!is_k && q_fp8 != NULL) {
+                uint8_t *out = q_fp8 + (t * num_heads + hh) * HEAD_DIM;
+                for (int i = 0; i < HEAD_DIM; ++i) {
+                    uint16_t codes[MAX_CAND];
+                    int nc = 0;
+                    out[i] = dspark_oracle_fp8_store(kcode[i], q_scale);
+                    for (int q = 0; q < ncand_k[i]; ++q)
+                        nc = add_candidate(codes, nc, dspark_oracle_fp8_store(kcand[i][q], q_scale));
+                    record_alternates(&n_alt, alt_capacity, 2,
+                                      (t * num_heads + hh) * HEAD_DIM + i, codes, nc,
+                                      alt_tag, alt_index, alt_count, alt_codes);
+                }
+            }
+            if (is_k && slot >= 0) {
+                int h = hh - num_heads;
+                int64_t crow = ((slot / block_size * nkv + h) * block_size + slot % block_size) *
+                               (2 * HEAD_DIM);
+                for (int i = 0; i < HEAD_DIM; ++i) {
+                    uint16_t codes[MAX_CAND];
+                    int nc = 0;
+                    if (fp8) {
+                        ((uint8_t *)cache)[crow + i] = dspark_oracle_fp8_store(kcode[i], k_scale);
+                        for (int q = 0; q < ncand_k[i]; ++q)
+                            nc = add_candidate(codes, nc, dspark_oracle_fp8_store(kcand[i][q], k_scale));
+                    } else {
+                        ((uint16_t *)cache)[crow + i] = kcode[i];
+                        for (int q = 0; q < ncand_k[i]; ++q)
+                            nc = add_candidate(codes, nc, kcand[i][q]);
                     }
+                    record_alternates(&n_alt, alt_capacity, 1, crow + i, codes, nc, alt_tag,
+                                      alt_index, alt_count, alt_codes);
+                }
+            }
+        }
+        /* v heads: stored as they are */
+        if (slot >= 0) {
+            for (int h = 0; h < nkv; ++h) {
+                const uint16_t *vrow = tok + (int64_t)(num_heads + nkv + h) * HEAD_DIM;
+                int64_t crow = ((slot / block_size * nkv + h) * block_size + slot % block_size) *
+                               (2 * HEAD_DIM) + HEAD_DIM;
+                for (int i = 0; i < HEAD_DIM; ++i) {
+                    if (fp8)
+                        ((uint8_t *)cache)[crow + i] = dspark_oracle_fp8_store(vrow[i], v_scale);
+                    else
+                        ((uint16_t *)cache)[crow + i] = vrow[i];
                 }
             }
         }

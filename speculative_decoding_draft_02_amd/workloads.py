@@ -273,3 +273,139 @@ def custom(num_ctx, num_layers, num_kv_heads, rotary_dim, block_size, num_blocks
     cs = rope_table(rows, rotary_dim)
     return Workload("custom", N, L, nkv, rotary_dim, block_size, num_blocks, fp8, eps,
                     all_kv, w, positions, slots, cs, ks, vs)
+
+
+# ----------------------------------------------------------------------------
+# The draft block's fused QK-norm / RoPE / KV insert: qkv [T, (H + 2 nkv) * 128]
+# for T = requests x 7 query rows (the draft block of the vLLM API page
+# "vllm.models.minimax_m3.common.dspark"), each request's rows at consecutive
+# positions after its context, stored at the slots its block table gives.
+
+DRAFT_ROWS = 7
+
+@dataclass
+class InsertWorkload:
+    name: str
+    num_tokens: int
+    num_heads: int
+    num_kv_heads: int
+    rotary_dim: int
+    block_size: int
+    num_blocks: int
+    fp8: bool                  # fp8 e4m3 cache (else bf16)
+    q_fp8: bool                # the e4m3 query output is requested
+    eps: float
+    qkv: np.ndarray            # uint16 bf16 bits [T, (H + 2 nkv) * 128]
+    q_norm_weight: np.ndarray  # uint16 bf16 bits [128]
+    k_norm_weight: np.ndarray  # uint16 bf16 bits [128]
+    positions: np.ndarray      # int64 [T]
+    slot_mapping: np.ndarray | None   # int64 [T] (< 0 = not stored) or None (no insert)
+    cos_sin: np.ndarray        # uint16 bf16 bits [rows, R]
+    k_scale: float
+    v_scale: float
+    q_scale: float
+
+    @property
+    def heads_per_token(self) -> int:
+        return self.num_heads + 2 * self.num_kv_heads
+
+    @property
+    def sentinel(self) -> int:
+        return SENTINEL_FP8 if self.fp8 else SENTINEL_BF16
+
+    @property
+    def cache_shape(self):
+        return (self.num_blocks, self.num_kv_heads, self.block_size, 2 * HEAD_DIM)
+
+    def new_host_cache(self) -> np.ndarray:
+        return np.full(self.cache_shape, self.sentinel, dtype=np.uint8 if self.fp8 else np.uint16)
+
+    def stored_tokens(self) -> int:
+        return 0 if self.slot_mapping is None else int(np.count_nonzero(self.slot_mapping >= 0))
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the op must move: qkv read, its query and key heads written
+        back, the stored tokens' K/V cache rows, the q fp8 output, each
+        token's cos/sin row, position and slot, and the two norm weights."""
+        T, H, nkv, R = self.num_tokens, self.num_heads, self.num_kv_heads, self.rotary_dim
+        e = 1 if self.fp8 else 2
+        b = T * (self.heads_per_token * HEAD_DIM * 2 + (H + nkv) * HEAD_DIM * 2 + 2 * R + 8)
+        if self.slot_mapping is not None:
+            b += 8 * T + self.stored_tokens() * 2 * nkv * HEAD_DIM * e
+        if self.q_fp8:
+            b += T * H * HEAD_DIM
+        return b + 2 * HEAD_DIM * 2
+
+
+INSERT_NAMES = ["insert_tiny", "insert_draft_bf16", "insert_draft_fp8"]
+
+INSERT_DESCRIPTIONS = [
+    "3 requests x 7 rows, H=4 nkv=2 R=64 bs=16 8 blocks bf16 cache, q fp8 out, 1 padded row",
+    "64 requests x 7 rows (448 tokens), H=32 nkv=8 R=64 bs=64 512 blocks bf16 cache, 2% padding",
+    "64 requests x 7 rows (448 tokens), H=32 nkv=8 R=64 bs=64 512 blocks fp8 e4m3 cache "
+    "with k/v scales, q fp8 out, 2% padding",
+]
+
+
+def _draft_block(rng, reqs, bs, nb, max_pos):
+    """Positions and slots of `reqs` requests' draft rows: request r's rows
+    sit at p0_r .. p0_r + 6 and at the slots of its own random blocks."""
+    p0 = rng.integers(0, max_pos - DRAFT_ROWS + 1, size=reqs)
+    free_blocks = list(rng.permutation(nb))
+    pos_list, slot_list = [], []
+    for r in range(reqs):
+        p = np.arange(p0[r], p0[r] + DRAFT_ROWS, dtype=np.int64)
+        logical = p // bs
+        first = int(logical[0])
+        table = [int(free_blocks.pop()) for _ in range(int(logical[-1]) - first + 1)]
+        slot_list.append(np.array([table[int(lb) - first] for lb in logical], np.int64) * bs + p % bs)
+        pos_list.append(p)
+    return np.concatenate(pos_list), np.concatenate(slot_list)
+
+
+def insert_make(index: int, variant: int = 0) -> InsertWorkload:
+    """Draft-block workload ``index`` (0..2, in the order of INSERT_NAMES)."""
+    rng = np.random.default_rng(2000 + index + 7919 * variant)
+    if index == 0:
+        reqs, H, nkv, R, bs, nb, fp8, qf, std, rows = 3, 4, 2, 64, 16, 8, False, True, 1.0, 4096
+    elif index in (1, 2):
+        fp8 = index == 2
+        reqs, H, nkv, R, bs, nb, qf, std, rows = 64, 32, 8, 64, 64, 512, fp8, 4.0 if fp8 else 1.0, 131072
+    else:
+        raise ValueError("insert workload index must be 0..2")
+    T = reqs * DRAFT_ROWS
+    qkv = _normal_bf16(rng, (T, (H + 2 * nkv) * HEAD_DIM), std)
+    qw = _normal_bf16(rng, (HEAD_DIM,), 0.1)
+    kw = _normal_bf16(rng, (HEAD_DIM,), 0.1)
+    positions, slots = _draft_block(rng, reqs, bs, nb, rows)
+    slots = _pad(rng, slots, 1 if index == 0 else int(round(0.02 * T)))
+    ks, vs, qs = 1.0, 1.0, 1.0
+    if fp8:
+        ks, vs = (float(np.float32(x)) for x in rng.uniform(0.05, 0.5, size=2))
+    if qf:
+        qs = float(np.float32(rng.uniform(0.05, 0.5)))
+    return InsertWorkload(INSERT_NAMES[index], T, H, nkv, R, bs, nb, fp8, qf, 1e-6, qkv, qw, kw,
+                          positions, slots, rope_table(rows, R), ks, vs, qs)
+
+
+def insert_custom(num_tokens, num_heads, num_kv_heads, rotary_dim, block_size, num_blocks, fp8,
+                  q_fp8, seed, pad_fraction=0.1, std=1.0, insert=True, cs_rows=None,
+                  eps=1e-6) -> InsertWorkload:
+    """A small draft-block workload of arbitrary shape with unique random slots."""
+    rng = np.random.default_rng(seed)
+    T, H, nkv = num_tokens, num_heads, num_kv_heads
+    assert not insert or T <= num_blocks * block_size
+    qkv = _normal_bf16(rng, (T, (H + 2 * nkv) * HEAD_DIM), std)
+    qw = _normal_bf16(rng, (HEAD_DIM,), 0.1)
+    kw = _normal_bf16(rng, (HEAD_DIM,), 0.1)
+    rows = cs_rows if cs_rows is not None else max(T, 1) + 64
+    positions = rng.integers(0, rows, size=T).astype(np.int64)
+    slots = None
+    if insert:
+        slots = rng.permutation(num_blocks * block_size)[:T].astype(np.int64)
+        slots = _pad(rng, slots, int(round(pad_fraction * T)))
+    ks, vs = (float(np.float32(x)) for x in rng.uniform(0.05, 0.5, size=2)) if fp8 else (1.0, 1.0)
+    qs = float(np.float32(rng.uniform(0.05, 0.5))) if q_fp8 else 1.0
+    return InsertWorkload("insert_custom", T, H, nkv, rotary_dim, block_size, num_blocks, fp8,
+                          q_fp8, eps, qkv, qw, kw, positions, slots, rope_table(rows, rotary_dim),
+                          ks, vs, qs)

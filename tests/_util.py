@@ -117,3 +117,72 @@ def torch_unfused(wl: W.Workload):
             flat[rows, :128] = kb[:, h]
             flat[rows, 128:] = vb[:, h]
     return caches
+
+
+# ------------------------------------------------------------------------
+# The draft block's QK-norm / RoPE / KV insert, written independently with
+# PyTorch CPU ops in fp32 from its description on the vLLM API page
+# "vllm.models.minimax_m3.common.dspark" (dspark_qknorm_rope_kv_insert): the
+# per-head Gemma RMSNorm of the query heads (q weight) and key heads (k
+# weight), rounded to bf16; NeoX RoPE on the leading R dims, rounded to bf16;
+# the key and value heads of every token with slot >= 0 stored as
+# reshape_and_cache_flash would; the rotated queries as e4m3 of q / q_scale.
+
+def torch_insert(wl):
+    """Returns (qkv uint16 [T, W], cache or None, q_fp8 uint8 or None)."""
+    T, H, nkv, R = wl.num_tokens, wl.num_heads, wl.num_kv_heads, wl.rotary_dim
+    x = torch.from_numpy(wl.qkv.view(np.int16)).view(torch.bfloat16).view(T, H + 2 * nkv, HEAD_DIM)
+    qw = torch.from_numpy(wl.q_norm_weight.view(np.int16)).view(torch.bfloat16).float()
+    kw = torch.from_numpy(wl.k_norm_weight.view(np.int16)).view(torch.bfloat16).float()
+
+    def norm(h, w):
+        hf = h.float()
+        var = hf.pow(2).mean(dim=-1, keepdim=True)
+        return (hf * torch.rsqrt(var + wl.eps) * (1.0 + w)).to(torch.bfloat16)
+
+    cs = torch.from_numpy(wl.cos_sin.view(np.int16)).view(torch.bfloat16)
+    pos = torch.from_numpy(wl.positions)
+    cos = cs[pos, : R // 2].float().view(T, 1, R // 2)
+    sin = cs[pos, R // 2:].float().view(T, 1, R // 2)
+
+    def rope(y):
+        x1, x2 = y[..., : R // 2].float(), y[..., R // 2: R].float()
+        return torch.cat([(x1 * cos - x2 * sin).to(torch.bfloat16),
+                          (x2 * cos + x1 * sin).to(torch.bfloat16), y[..., R:]], dim=-1)
+
+    q = rope(norm(x[:, :H], qw))
+    k = rope(norm(x[:, H:H + nkv], kw))
+    v = x[:, H + nkv:]
+    out = torch.cat([q, k, v], dim=1).reshape(T, -1).view(torch.int16).numpy().view(np.uint16).copy()
+
+    def e4m3(t, s):
+        return (t.float() / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    qf = e4m3(q, wl.q_scale).reshape(T, -1).numpy().copy() if wl.q_fp8 else None
+    cache = None
+    if wl.slot_mapping is not None:
+        cache = wl.new_host_cache()
+        slots = torch.from_numpy(wl.slot_mapping)
+        valid = torch.nonzero(slots >= 0).flatten()
+        s = slots[valid]
+        blk, off = s // wl.block_size, s % wl.block_size
+        if wl.fp8:
+            kb, vb = e4m3(k[valid], wl.k_scale), e4m3(v[valid], wl.v_scale)
+            flat = torch.from_numpy(cache.reshape(-1, 256))
+        else:
+            kb, vb = k[valid].view(torch.int16), v[valid].view(torch.int16)
+            flat = torch.from_numpy(cache.view(np.int16).reshape(-1, 256))
+        for h in range(nkv):
+            rows = (blk * nkv + h) * wl.block_size + off
+            flat[rows, :128] = kb[:, h]
+            flat[rows, 128:] = vb[:, h]
+    return out, cache, qf
+
+
+def run_insert_oracle(oracle, wl, **kw):
+    cache = wl.new_host_cache() if wl.slot_mapping is not None else None
+    return oracle.qknorm_rope_kv_insert(
+        wl.qkv, wl.num_heads, wl.num_kv_heads, wl.q_norm_weight, wl.k_norm_weight, wl.eps,
+        wl.positions, wl.cos_sin, wl.rotary_dim, slot_mapping=wl.slot_mapping, cache=cache,
+        fp8=wl.fp8, k_scale=wl.k_scale, v_scale=wl.v_scale, want_q_fp8=wl.q_fp8,
+        q_scale=wl.q_scale, **kw)
