@@ -41,7 +41,11 @@ METRIC = "context-KV write HBM GB/s (% of MI355X peak) and token-layers/s"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["speculative_decoding_draft_02_amd/csrc/ctx_kv_kernel.hip",
                   "speculative_decoding_draft_02_amd/csrc/ctx_kv_writer.cpp",
-                  "speculative_decoding_draft_02_amd/csrc/ctx_kv_args.h"]
+                  "speculative_decoding_draft_02_amd/csrc/ctx_kv_args.h",
+                  "speculative_decoding_draft_02_amd/csrc/device_common.h",
+                  "speculative_decoding_draft_02_amd/csrc/qknorm_insert_kernel.hip",
+                  "speculative_decoding_draft_02_amd/csrc/qknorm_insert.cpp",
+                  "speculative_decoding_draft_02_amd/csrc/qknorm_insert_args.h"]
 HEADLINE = 1   # index of the prefill bf16 workload
 
 
@@ -122,6 +126,52 @@ class Setup:
             raise RuntimeError(_lib.dspark_ctx_kv_last_error())
 
 
+class InsertSetup:
+    """The draft block's QK-norm / RoPE / KV insert: `n_sets` independently
+    drawn draft blocks (qkv, positions, slots, q fp8 output) over one cache,
+    so that a cycle of launches streams more than the last-level cache
+    holds.  Every launch is one call of the C ABI."""
+
+    def __init__(self, index: int, n_sets: int, dev):
+        self.sets = [W.insert_make(index, variant=v) for v in range(n_sets)]
+        wl = self.sets[0]
+        self.wl = wl
+        if wl.fp8:
+            self.cache = torch.full(wl.cache_shape, 0xFF, dtype=torch.uint8, device=dev)
+        else:
+            self.cache = torch.full(wl.cache_shape, -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        self.ks = torch.tensor([wl.k_scale], dtype=torch.float32, device=dev)
+        self.vs = torch.tensor([wl.v_scale], dtype=torch.float32, device=dev)
+        self.qw = bf16_dev(wl.q_norm_weight, dev)
+        self.kw = bf16_dev(wl.k_norm_weight, dev)
+        self.cs = bf16_dev(wl.cos_sin, dev)
+        self.inputs = []
+        for s in self.sets:
+            self.inputs.append(dict(
+                qkv=bf16_dev(s.qkv, dev), positions=torch.from_numpy(s.positions).to(dev),
+                slots=torch.from_numpy(s.slot_mapping).to(dev),
+                qf=torch.empty((s.num_tokens, s.num_heads * 128), dtype=torch.uint8, device=dev)
+                if s.q_fp8 else None))
+        self.bytes = [s.algorithmic_bytes() for s in self.sets]
+        self.token_layers = [s.num_tokens for s in self.sets]
+        lib = _lib.load()
+        self._call = lib.dspark_qknorm_rope_kv_insert
+        self._args = [(i["qkv"].data_ptr(), wl.num_tokens, self.qw.data_ptr(), self.kw.data_ptr(),
+                       self.cs.data_ptr(), self.cs.shape[0], i["positions"].data_ptr(),
+                       wl.num_heads, wl.num_kv_heads, wl.rotary_dim, wl.eps,
+                       i["slots"].data_ptr(), self.cache.data_ptr(), wl.num_blocks,
+                       wl.block_size, _lib.KV_FP8_E4M3 if wl.fp8 else _lib.KV_AUTO,
+                       self.ks.data_ptr() if wl.fp8 else None,
+                       self.vs.data_ptr() if wl.fp8 else None,
+                       i["qf"].data_ptr() if i["qf"] is not None else None, wl.q_scale)
+                      for i in self.inputs]
+
+    def launch(self, k: int, stream_ptr) -> None:
+        st = self._call(*self._args[k % len(self._args)], stream_ptr)
+        if st != _lib.OK:
+            raise RuntimeError(_lib.dspark_ctx_kv_last_error())
+
+
 def time_eager(setup: Setup, steps: int, warmup: int, stream):
     """Warm up, then time exactly `steps` back-to-back launches with one HIP
     event pair around the region on the launch stream.  A second, untimed
@@ -157,15 +207,16 @@ def time_eager(setup: Setup, steps: int, warmup: int, stream):
     return dict(region_s=region, wall_s=wall, single_s=per, bytes=nbytes, token_layers=ntl)
 
 
-def time_graph(setup: Setup, steps: int, warmup: int, stream, per_graph: int = 50):
-    """Capture `per_graph` writes in one HIP graph and replay it until
-    `steps` writes have run; per-call time = region / steps."""
+def time_graph(setup, steps: int, warmup: int, stream, per_graph: int = 50):
+    """Capture `per_graph` writes in one HIP graph (rotating over the setup's
+    input sets) and replay it until `steps` writes have run; per-call time =
+    region / steps."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
             sp = torch.cuda.current_stream().cuda_stream
-            for _ in range(per_graph):
-                setup.launch(0, sp)
+            for k in range(per_graph):
+                setup.launch(k, sp)
         for _ in range(max(1, warmup // per_graph)):
             g.replay()
         replays = max(1, steps // per_graph)
@@ -180,8 +231,10 @@ def time_graph(setup: Setup, steps: int, warmup: int, stream, per_graph: int = 5
     region = start.elapsed_time(end) * 1e-3
     del g
     n = replays * per_graph
-    return dict(region_s=region, per_call_s=region / n, calls=n, bytes=setup.bytes[0],
-                token_layers=setup.token_layers[0])
+    nb = [setup.bytes[k % len(setup.bytes)] for k in range(per_graph)]
+    ntl = [setup.token_layers[k % len(setup.bytes)] for k in range(per_graph)]
+    return dict(region_s=region, per_call_s=region / n, calls=n, bytes=float(np.mean(nb)),
+                token_layers=float(np.mean(ntl)))
 
 
 def copy_reference(dev, stream, nbytes: int = 82_214_912, reps: int = 50):
@@ -207,6 +260,35 @@ def copy_reference(dev, stream, nbytes: int = 82_214_912, reps: int = 50):
     del src, dst
     return {"bytes_read_plus_written": 2 * nbytes, "us": t * 1e6, "GB_s": 2 * nbytes / t / 1e9,
             "how": "torch copy_ of %d bytes, 4 buffer pairs rotated, %d copies" % (nbytes, reps)}
+
+
+def small_copy_reference(nbytes_moved: float, n_bufs: int, stream, per_graph: int = 64,
+                         replays: int = 16):
+    """Graph-replayed device copies that read and write nbytes_moved / 2
+    bytes each, over n_bufs rotated buffer pairs: what a plain stream of the
+    same size achieves, the practical ceiling of a small launch."""
+    n = int(nbytes_moved // 2) // 16 * 16
+    dev = torch.device("cuda:0")
+    src = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(n_bufs)]
+    dst = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(n_bufs)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(per_graph):
+                dst[k % n_bufs].copy_(src[k % n_bufs])
+        g.replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(replays):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+    t = start.elapsed_time(end) * 1e-3 / (replays * per_graph)
+    del g, src, dst
+    return {"us_per_copy": t * 1e6, "GB_s": 2 * n / t / 1e9,
+            "how": "torch copy_ of %d bytes under HIP-graph replay, %d buffer pairs" % (n, n_bufs)}
 
 
 def cpu_baseline(index: int, budget_s: float = 12.0):
@@ -255,7 +337,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all"] + W.NAMES)
+    ap.add_argument("--workload", default="all", choices=["all", "insert"] + W.NAMES)
+    ap.add_argument("--insert-sets", type=int, default=32,
+                    help="draft blocks rotated in the insert's graph")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -288,7 +372,7 @@ def main():
     reference_copy = copy_reference(dev, stream)
     log("reference copy", json.dumps(reference_copy))
 
-    names = W.NAMES if args.workload == "all" else [args.workload]
+    names = W.NAMES if args.workload == "all" else [n for n in W.NAMES if n == args.workload]
     results = {}
     for name in names:
         index = W.NAMES.index(name)
@@ -347,6 +431,29 @@ def main():
         del setup
         torch.cuda.empty_cache()
 
+    if args.workload in ("all", "insert"):
+        # the draft block's fused QK-norm / RoPE / KV insert (448 draft rows)
+        for index in (1, 2):
+            name = W.INSERT_NAMES[index]
+            log("workload", name, "setup")
+            setup = InsertSetup(index, args.insert_sets, dev)
+            r = time_graph(setup, max(args.steps, 1000), args.warmup, stream,
+                           per_graph=2 * args.insert_sets)
+            per = r["per_call_s"]
+            results[name] = {"us_per_call": per * 1e6, "GB_s": r["bytes"] / per / 1e9,
+                             "tokens_per_s": r["token_layers"] / per,
+                             "timing": "%d calls as HIP-graph replays over %d draft blocks"
+                                       % (r["calls"], args.insert_sets),
+                             "bytes_per_call": r["bytes"],
+                             "config": W.INSERT_DESCRIPTIONS[index]}
+            results[name]["pct_of_hbm_peak"] = 100.0 * results[name]["GB_s"] / HBM_PEAK_GBS
+            ref = small_copy_reference(r["bytes"], args.insert_sets, stream)
+            results[name]["same_size_copy"] = ref
+            results[name]["pct_of_same_size_copy"] = 100.0 * results[name]["GB_s"] / ref["GB_s"]
+            log(name, json.dumps(results[name]))
+            del setup
+            torch.cuda.empty_cache()
+
     head = W.NAMES[HEADLINE]
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
@@ -370,13 +477,16 @@ def main():
         name = next(iter(results))
         out.update({"value": results[name]["GB_s"],
                     "ms_per_step": results[name].get("ms_per_step", results[name].get("us_per_call", 0) / 1e3)})
-        out["config"] = {"workload": name + ": " + W.DESCRIPTIONS[W.NAMES.index(name)]}
+        desc = (W.DESCRIPTIONS[W.NAMES.index(name)] if name in W.NAMES
+                else W.INSERT_DESCRIPTIONS[W.INSERT_NAMES.index(name)])
+        out["config"] = {"workload": name + ": " + desc}
         out["roofline"] = None
     out["workloads"] = results
     out["reference_copy"] = reference_copy
-    if not args.no_cpu_baseline:
+    ctx_names = [n for n in results if n in W.NAMES]
+    if not args.no_cpu_baseline and ctx_names:
         log("cpu baseline (oracle)")
-        cb_index = HEADLINE if head in results else W.NAMES.index(next(iter(results)))
+        cb_index = HEADLINE if head in results else W.NAMES.index(ctx_names[0])
         out["cpu_baseline"] = cpu_baseline(cb_index)
     else:
         out["cpu_baseline"] = None

@@ -1,4 +1,5 @@
-"""ctypes binding of libdspark_ctx_kv.so (include/dspark_ctx_kv.h).
+"""ctypes binding of libdspark_ctx_kv.so (include/dspark_ctx_kv.h and
+include/dspark_qknorm_insert.h).
 
 Argument marshalling only: every function here has the name and argument
 order of the C entry point it calls, takes device pointers as Python ints,
@@ -36,6 +37,9 @@ SIGNATURES = {
     "dspark_ctx_kv_writer_destroy": ([_P], None),
     "dspark_rotary_dims_supported": ([_I32, _I32], ctypes.c_int),
     "dspark_ctx_kv_last_error": ([], ctypes.c_char_p),
+    "dspark_qknorm_rope_kv_insert": ([_P, _I64, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                      ctypes.c_float, _P, _P, _I64, _I32, _I32, _P, _P, _P,
+                                      ctypes.c_float, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -112,3 +116,13 @@ def dspark_rotary_dims_supported(rotary_dim, head_dim) -> int:
 
 def dspark_ctx_kv_last_error() -> str:
     return load().dspark_ctx_kv_last_error().decode()
+
+
+def dspark_qknorm_rope_kv_insert(qkv, num_tokens, q_norm_weight, k_norm_weight, cos_sin_cache,
+                                 cos_sin_rows, positions, num_heads, num_kv_heads, rotary_dim, eps,
+                                 slot_mapping, kv_cache, num_blocks, block_size, kv_cache_dtype,
+                                 k_scale, v_scale, q_fp8_out, q_fp8_scale, stream) -> int:
+    return load().dspark_qknorm_rope_kv_insert(
+        qkv, num_tokens, q_norm_weight, k_norm_weight, cos_sin_cache, cos_sin_rows, positions,
+        num_heads, num_kv_heads, rotary_dim, eps, slot_mapping, kv_cache, num_blocks, block_size,
+        kv_cache_dtype, k_scale, v_scale, q_fp8_out, q_fp8_scale, stream)

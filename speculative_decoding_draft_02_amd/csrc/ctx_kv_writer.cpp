@@ -18,6 +18,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "ctx_kv_args.h"
+#include "qknorm_insert_args.h"
 #include "dspark_ctx_kv.h"
 
 struct dspark_ctx_kv_writer {
@@ -35,11 +36,11 @@ struct dspark_ctx_kv_writer {
 };
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int status, const char *fmt, ...) {
+// The last-error string of every entry point of the library.
+int dspark::fail(int status, const char *fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -48,6 +49,10 @@ int fail(int status, const char *fmt, ...) {
     g_last_error = buf;
     return status;
 }
+
+namespace {
+
+using dspark::fail;
 
 int ok() { return DSPARK_OK; }
 

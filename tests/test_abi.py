@@ -12,7 +12,7 @@ import pytest
 from speculative_decoding_draft_02_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dspark_ctx_kv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("dspark_ctx_kv.h", "dspark_qknorm_insert.h")]
 
 
 @pytest.fixture(scope="module")
@@ -24,7 +24,9 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    assert sorted(HEADERS) == sorted(
+        os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")))
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
 
@@ -229,3 +231,51 @@ def test_python_writer_splits_slot_mappings():
         _split_slot_mapping([a, None, a], 3)
     with pytest.raises(ValueError):
         _split_slot_mapping([a, a], 3)
+
+
+def test_qknorm_insert_argument_checks(lib):
+    """Every refusal happens on the host before a launch; num_tokens == 0 is
+    a no-op.  Fake pointers are never dereferenced."""
+    fake = BASE + 0x100000
+
+    def call(**kw):
+        a = dict(qkv=fake, num_tokens=7, q_norm_weight=fake, k_norm_weight=fake,
+                 cos_sin_cache=fake, cos_sin_rows=4096, positions=fake, num_heads=4,
+                 num_kv_heads=2, rotary_dim=64, eps=1e-6, slot_mapping=fake, kv_cache=fake,
+                 num_blocks=8, block_size=16, kv_cache_dtype=_lib.KV_AUTO, k_scale=None,
+                 v_scale=None, q_fp8_out=fake, q_fp8_scale=0.5, stream=None)
+        a.update(kw)
+        return _lib.dspark_qknorm_rope_kv_insert(*a.values())
+
+    for kw, reason in [
+        (dict(rotary_dim=48), "rotary_dim 48"),
+        (dict(num_tokens=-1), "negative"),
+        (dict(num_heads=0), "must be positive"),
+        (dict(num_kv_heads=-2), "must be positive"),
+        (dict(num_tokens=1 << 26, num_heads=32, num_kv_heads=8), "exceeds 2^31"),
+        (dict(qkv=0), "NULL"),
+        (dict(k_norm_weight=0), "NULL"),
+        (dict(qkv=fake + 8), "16-byte aligned"),
+        (dict(cos_sin_cache=fake + 2), "16-byte aligned"),
+        (dict(positions=fake + 4), "8-byte aligned"),
+        (dict(cos_sin_rows=0), "no rows"),
+        (dict(kv_cache=0), "without a KV cache"),
+        (dict(slot_mapping=fake + 4), "slot_mapping must be 8-byte aligned"),
+        (dict(kv_cache=fake + 8), "kv_cache must be 16-byte aligned"),
+        (dict(num_blocks=0), "no blocks"),
+        (dict(block_size=24), "block size 24 is not a power of two"),
+        (dict(kv_cache_dtype=3), "kv_cache_dtype 3"),
+        (dict(k_scale=fake + 2), "4-byte aligned"),
+        (dict(q_fp8_out=fake + 4), "q_fp8_out must be 8-byte aligned"),
+        (dict(q_fp8_scale=0.0), "q_fp8_scale"),
+        (dict(q_fp8_scale=float("inf")), "q_fp8_scale"),
+        (dict(q_fp8_scale=float("nan")), "q_fp8_scale"),
+    ]:
+        assert call(**kw) == _lib.E_ARG, kw
+        assert reason in _lib.dspark_ctx_kv_last_error(), (kw, _lib.dspark_ctx_kv_last_error())
+    # no slot mapping: the cache arguments are not looked at
+    assert call(num_tokens=0, slot_mapping=None, kv_cache=0, num_blocks=0, block_size=3,
+                kv_cache_dtype=9) == _lib.OK
+    # no q fp8 output: its scale is not looked at
+    assert call(num_tokens=0, q_fp8_out=None, q_fp8_scale=0.0) == _lib.OK
+    assert call(num_tokens=0) == _lib.OK
