@@ -262,6 +262,87 @@ def copy_reference(dev, stream, nbytes: int = 82_214_912, reps: int = 50):
             "how": "torch copy_ of %d bytes, 4 buffer pairs rotated, %d copies" % (nbytes, reps)}
 
 
+def unfused_write(all_kv, k_norm_weight, eps, positions, cos_sin, rotary_dim, slot_mapping,
+                  caches, fp8, k_scales, v_scales):
+    """The base path the fused write replaces (vLLM API page
+    "vllm.models.minimax_m3.common.ops.dspark_context_kv", module docstring),
+    in PyTorch ops on the GPU: the permute copy, one Gemma K norm per layer and
+    a stack, positions.repeat, NeoX rotary on the stacked K, and one cache
+    write per layer.  A measurement comparator (and a cross-check of the
+    oracle), never a fallback: the product path has none.  Unlike vLLM's
+    reshape_and_cache_flash kernel, the PyTorch cache write needs the valid
+    token list, so this chain syncs once per call (torch.nonzero)."""
+    N, L, _, H, D = all_kv.shape
+    R = rotary_dim
+    all_k = all_kv[:, :, 0].permute(1, 0, 2, 3).contiguous()       # [L, N, H, D]
+    all_v = all_kv[:, :, 1].permute(1, 0, 2, 3).contiguous()
+    normed = []
+    for l in range(L):
+        x = all_k[l].float()
+        var = x.pow(2).mean(dim=-1, keepdim=True)
+        normed.append((x * torch.rsqrt(var + eps) * (1.0 + k_norm_weight[l].float()))
+                      .to(torch.bfloat16))
+    k = torch.stack(normed).view(L * N, H, D)
+    pos = positions.repeat(L)
+    cs = cos_sin[pos]
+    cos = cs[:, : R // 2].float().unsqueeze(1)
+    sin = cs[:, R // 2:].float().unsqueeze(1)
+    x1 = k[..., : R // 2].float()
+    x2 = k[..., R // 2: R].float()
+    k[..., : R // 2] = (x1 * cos - x2 * sin).to(torch.bfloat16)
+    k[..., R // 2: R] = (x2 * cos + x1 * sin).to(torch.bfloat16)
+    k = k.view(L, N, H, D)
+    valid = torch.nonzero(slot_mapping >= 0).squeeze(1)
+    s = slot_mapping[valid]
+    bs = caches[0].shape[2]
+    heads = torch.arange(H, device=s.device)
+    rows = ((s // bs)[:, None] * H + heads[None, :]) * bs + (s % bs)[:, None]   # [V, H]
+    rows = rows.reshape(-1)
+    for l in range(L):
+        kk = k[l, valid].reshape(-1, D)
+        vv = all_v[l, valid].reshape(-1, D)
+        if fp8:
+            kk = (kk.float() / k_scales[l]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            vv = (vv.float() / v_scales[l]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        flat = caches[l].view(-1, 2 * D)
+        flat[rows] = torch.cat([kk, vv], dim=1)
+
+
+class UnfusedSetup:
+    """The same workload and input sets, written by the unfused PyTorch chain."""
+
+    def __init__(self, setup: "Setup", dev):
+        self.s = setup
+        self.caches = [a.kv_cache for a in setup.layers]
+        self.ks = [a._k_scale for a in setup.layers]
+        self.vs = [a._v_scale for a in setup.layers]
+        self.bytes = setup.bytes
+        self.token_layers = setup.token_layers
+
+    def launch(self, k: int, stream_ptr) -> None:
+        wl = self.s.wl
+        i = self.s.inputs[k % len(self.s.inputs)]
+        unfused_write(i["all_kv"], i["w"], wl.eps, i["positions"], i["cos_sin"], wl.rotary_dim,
+                      i["slots"], self.caches, wl.fp8, self.ks, self.vs)
+
+
+def time_unfused(setup: UnfusedSetup, steps: int, warmup: int, stream):
+    """Wall-clock-free timing of the unfused chain: HIP events around `steps`
+    calls on the stream (each call syncs once for its valid-token list)."""
+    with torch.cuda.stream(stream):
+        for k in range(warmup):
+            setup.launch(k, None)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            setup.launch(warmup + k, None)
+        end.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
 def small_copy_reference(nbytes_moved: float, n_bufs: int, stream, per_graph: int = 64,
                          replays: int = 16):
     """Graph-replayed device copies that read and write nbytes_moved / 2
@@ -291,32 +372,63 @@ def small_copy_reference(nbytes_moved: float, n_bufs: int, stream, per_graph: in
             "how": "torch copy_ of %d bytes under HIP-graph replay, %d buffer pairs" % (n, n_bufs)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(index: int, budget_s: float = 12.0):
-    """The oracle, single-threaded on this host, on a bounded token sample of
-    the workload (test infrastructure: only this leg of the bench uses it)."""
+    """The oracle on this host's cores, on whole calls of the workload (test
+    infrastructure: only this leg of the bench uses it).  Single-threaded,
+    then with one contiguous token range per thread (the oracle's C code runs
+    with the GIL released), each timed over repeated whole calls for about
+    budget_s / 2 seconds."""
     sys.path.insert(0, ROOT)
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     oracle.build()
     wl = W.make(index)
     caches = wl.new_host_caches()
 
-    def run(t_end, t_begin=0):
-        t0 = time.perf_counter()
+    def run(t_begin, t_end):
         oracle.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
                             wl.rotary_dim, wl.slot_mapping, caches, wl.fp8, wl.k_scales,
                             wl.v_scales, t_begin=t_begin, t_end=t_end)
-        return time.perf_counter() - t0
 
-    # whole-workload calls, repeated until the budget is spent (at least one)
-    reps, total = 0, 0.0
-    while reps == 0 or total < budget_s:
-        total += run(wl.num_ctx)
-        reps += 1
-    nbytes = wl.algorithmic_bytes() * reps
-    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d whole call(s) of the %s workload (%d tokens), single thread, %.1f s"
-                      % (reps, wl.name, wl.num_ctx, total),
-            "token_layers_per_s": wl.token_layers() * reps / total}
+    def timed(threads):
+        bounds = np.linspace(0, wl.num_ctx, threads + 1).astype(int)
+        reps, total = 0, 0.0
+        with ThreadPoolExecutor(threads) as ex:
+            while reps == 0 or total < budget_s / 2:
+                t0 = time.perf_counter()
+                list(ex.map(lambda i: run(bounds[i], bounds[i + 1]), range(threads)))
+                total += time.perf_counter() - t0
+                reps += 1
+        return reps, total
+
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    threads = max(1, min(16, ncores))
+    r1, t1 = timed(1)
+    rn, tn = timed(threads)
+    b = wl.algorithmic_bytes()
+    return {"value": b * rn / tn / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole call(s) of the %s workload (%d tokens) on %d threads, one "
+                      "contiguous token range each, %.1f s; CPU %s"
+                      % (rn, wl.name, wl.num_ctx, threads, tn, cpu_model()),
+            "token_layers_per_s": wl.token_layers() * rn / tn,
+            "single_thread": {"value": b * r1 / t1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": "%d whole call(s), %.1f s" % (r1, t1),
+                              "token_layers_per_s": wl.token_layers() * r1 / t1}}
 
 
 def traffic_for(name: str):
@@ -342,6 +454,8 @@ def main():
                     help="draft blocks rotated in the insert's graph")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the unfused PyTorch chain")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -408,6 +522,15 @@ def main():
                 "wall_s": r["wall_s"],
             }
         results[name]["pct_of_hbm_peak"] = 100.0 * results[name].get("kernel_GB_s", results[name]["GB_s"]) / HBM_PEAK_GBS
+        if not args.no_unfused:
+            # the base path the fused write replaces, on the same inputs and caches
+            ut = time_unfused(UnfusedSetup(setup, dev), min(args.steps, 50), 3, stream)
+            fused_us = results[name].get("kernel_us_avg", results[name].get("us_per_call"))
+            results[name]["unfused_torch"] = {
+                "us_per_call": ut * 1e6, "speedup_of_fused": ut * 1e6 / fused_us,
+                "how": "permute copy, per-layer Gemma K norm + stack, positions.repeat, NeoX "
+                       "rotary, per-layer cache write, in PyTorch ops (one host sync per call "
+                       "for the valid-token list); eager, %d calls" % min(args.steps, 50)}
         log(name, json.dumps(results[name]))
         del setup
         torch.cuda.empty_cache()
