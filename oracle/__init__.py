@@ -1,5 +1,6 @@
-"""Exact-value CPU oracle for the DSpark fused context-KV write and the
-draft block's fused QK-norm / RoPE / KV insert.
+"""Exact-value CPU oracle for the DSpark fused context-KV write, the draft
+block's fused QK-norm / RoPE / KV insert, and the step before the write (the
+hidden norm and the token-major K/V projection).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The product
@@ -85,6 +86,11 @@ def lib():
             ctypes.c_double,             # near_delta
             P, P, P, P, i64]             # alt_tag, alt_index, alt_count, alt_codes, cap
         L.dspark_oracle_qknorm_rope_kv_insert.restype = i64
+        L.dspark_oracle_gemma_rms_norm.argtypes = [P, i64, i32, P, ctypes.c_float, P,
+                                                   ctypes.c_double, P, P, i64]
+        L.dspark_oracle_gemma_rms_norm.restype = i64
+        L.dspark_oracle_kv_project.argtypes = [P, i32, P, i64, i64, i64, i64, P, P, P]
+        L.dspark_oracle_kv_project.restype = None
         _lib = L
     return _lib
 
@@ -248,3 +254,47 @@ def qknorm_rope_kv_insert(qkv, num_heads, num_kv_heads, q_norm_weight, k_norm_we
             return InsertResult(out, cache if slot_mapping is not None else None, qf,
                                 a_tag[:n], a_index[:n], a_count[:n], a_codes[:n])
         cap = int(n)
+
+
+# ------------------------------------------------ the step before the write ----
+
+def gemma_rms_norm(x, w, eps, near_delta: float = NEAR_DELTA):
+    """Gemma RMSNorm of each row of x (uint16 bf16 bits [rows, dim]) with
+    weight w [dim]: returns (codes [rows, dim], near-tie flat indices, the
+    other bf16 neighbour of each)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rows, dim = x.shape
+    w = np.ascontiguousarray(w, dtype=np.uint16).reshape(dim)
+    out = np.empty_like(x)
+    cap = max(1024, x.size // 64)
+    while True:
+        idx = np.zeros(cap, np.int64)
+        other = np.zeros(cap, np.uint16)
+        n = lib().dspark_oracle_gemma_rms_norm(x.ctypes.data, rows, dim, w.ctypes.data, float(eps),
+                                               out.ctypes.data, float(near_delta), idx.ctypes.data,
+                                               other.ctypes.data, cap)
+        if n <= cap:
+            return out, idx[:n], other[:n]
+        cap = int(n)
+
+
+def kv_project(z, W, rows=None, cols=None, want_sums: bool = False):
+    """bf16 of the exact products z @ W.T for the row range `rows` and column
+    range `cols` (each a (begin, end) pair, default all).  z: uint16 [N,
+    hidden], W: uint16 [C, hidden].  Returns the codes [r, c] and, with
+    want_sums, also the fp64 sums and sums of |products|."""
+    z = np.ascontiguousarray(z, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    N, hidden = z.shape
+    C, h2 = W.shape
+    assert h2 == hidden
+    r0, r1 = rows if rows is not None else (0, N)
+    c0, c1 = cols if cols is not None else (0, C)
+    assert 0 <= r0 <= r1 <= N and 0 <= c0 <= c1 <= C
+    out = np.empty((r1 - r0, c1 - c0), np.uint16)
+    ex = np.empty(out.shape, np.float64) if want_sums else None
+    ab = np.empty(out.shape, np.float64) if want_sums else None
+    lib().dspark_oracle_kv_project(z.ctypes.data, hidden, W.ctypes.data, r0, r1, c0, c1,
+                                   out.ctypes.data, ex.ctypes.data if want_sums else None,
+                                   ab.ctypes.data if want_sums else None)
+    return (out, ex, ab) if want_sums else out

@@ -49,6 +49,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---------------------------------------------------------------- bf16 --- */
@@ -501,4 +502,105 @@ int64_t dspark_oracle_qknorm_rope_kv_insert(
         }
     }
     return n_alt;
+}
+
+/* ------------------------------------------- the step before the write --- */
+
+/*
+ * Gemma RMSNorm of `rows` rows of `dim` bf16 values (the draft's hidden_norm
+ * on the context states, vLLM API page "vllm.models.minimax_m3.common.dspark":
+ * _gemma_rms_norm, _normalize_context_states):
+ *
+ *   out[r, i] = bf16( x[r, i] * rsqrt(mean_i(x[r, i]^2) + eps) * (1 + w[i]) )
+ *
+ * evaluated in fp64 and rounded once (the same reading of "fp32" as for the
+ * K norm).  An element within near_delta (relative) of a bf16 midpoint is a
+ * near tie: its flat index and the other neighbour are recorded (at most
+ * alt_capacity of them).  Returns the number of near ties.
+ */
+int64_t dspark_oracle_gemma_rms_norm(const uint16_t *x, int64_t rows, int32_t dim,
+                                     const uint16_t *w, float eps, uint16_t *out,
+                                     double near_delta, int64_t *alt_index,
+                                     uint16_t *alt_other, int64_t alt_capacity)
+{
+    int64_t n_alt = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * dim;
+        double ss = 0.0;
+        for (int i = 0; i < dim; ++i) {
+            double v = dspark_oracle_bf16_decode(xr[i]);
+            ss += v * v;
+        }
+        double rs = 1.0 / sqrt(ss / dim + (double)eps);
+        for (int i = 0; i < dim; ++i) {
+            double z = dspark_oracle_bf16_decode(xr[i]) * rs * (1.0 + dspark_oracle_bf16_decode(w[i]));
+            int near = 0;
+            uint16_t other = 0;
+            out[r * dim + i] = dspark_oracle_bf16_round(z, near_delta, &near, &other);
+            if (near) {
+                if (n_alt < alt_capacity) {
+                    alt_index[n_alt] = r * dim + i;
+                    alt_other[n_alt] = other;
+                }
+                ++n_alt;
+            }
+        }
+    }
+    return n_alt;
+}
+
+/*
+ * The token-major K/V projection (_project_context_kv_token_major on the same
+ * page): all_kv[t, c] = bf16( sum_k z[t, k] * W[c, k] ) for the rows
+ * [r_begin, r_end) and columns [c_begin, c_end) of the output, where z is
+ * [rows, hidden] (the hidden_norm output) and W is [cols, hidden] (a linear
+ * layer's [out, in] weight); column c = ((l * 2 + kv) * nkv + h) * 128 + d,
+ * so the output read as [rows, L, 2, nkv, 128] is all_kv.
+ *
+ * Products of bf16 values are exact in fp64 and the sum's rounding error is
+ * below hidden * 2^-53 of sum |z W|, so the value rounded to bf16 is the
+ * exactly rounded sum (a tie decided by that error is not possible unless
+ * the sum lies within ~2^-40 relative of a midpoint).  out, and exact /
+ * abs_sum when not NULL, are the selected block [r_end - r_begin,
+ * c_end - c_begin], row-major: the bf16 code, the fp64 sum and sum |z W| (for
+ * error bounds of fp32 accumulation).
+ */
+void dspark_oracle_kv_project(const uint16_t *z, int32_t hidden, const uint16_t *W,
+                              int64_t r_begin, int64_t r_end, int64_t c_begin, int64_t c_end,
+                              uint16_t *out, double *exact, double *abs_sum)
+{
+    const int64_t bc = c_end - c_begin;
+    const int64_t br = r_end - r_begin;
+    /* the block's z rows and one W row at a time, decoded to fp64 */
+    double *zd = (double *)malloc(sizeof(double) * (size_t)(br * hidden + 1));
+    double *wc = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!zd || !wc) {
+        free(zd);
+        free(wc);
+        return;
+    }
+    for (int64_t r = r_begin; r < r_end; ++r)
+        for (int k = 0; k < hidden; ++k)
+            zd[(r - r_begin) * hidden + k] = dspark_oracle_bf16_decode(z[r * hidden + k]);
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        for (int k = 0; k < hidden; ++k)
+            wc[k] = dspark_oracle_bf16_decode(W[c * hidden + k]);
+        for (int64_t r = r_begin; r < r_end; ++r) {
+            const double *zp = zd + (r - r_begin) * hidden;
+            double s = 0.0, a = 0.0;
+            for (int k = 0; k < hidden; ++k) {
+                double p = zp[k] * wc[k];
+                s += p;
+                a += fabs(p);
+            }
+            const int64_t o = (r - r_begin) * bc + (c - c_begin);
+            out[o] = dspark_oracle_bf16_round(s, 0.0, NULL, NULL);
+            if (exact)
+                exact[o] = s;
+            if (abs_sum)
+                abs_sum[o] = a;
+        }
+    }
+    free(zd);
+    free(wc);
 }

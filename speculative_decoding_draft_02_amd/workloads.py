@@ -409,3 +409,129 @@ def insert_custom(num_tokens, num_heads, num_kv_heads, rotary_dim, block_size, n
     return InsertWorkload("insert_custom", T, H, nkv, rotary_dim, block_size, num_blocks, fp8,
                           q_fp8, eps, qkv, qw, kw, positions, slots, rope_table(rows, rotary_dim),
                           ks, vs, qs)
+
+
+# ----------------------------------------------------------------------------
+# The step before the write: hidden_norm on the context states and the
+# token-major K/V projection (vLLM API page "vllm.models.minimax_m3.common.dspark":
+# _normalize_context_states, _project_context_kv_token_major), whose output
+# all_kv [N, L, 2, nkv, 128] the write consumes.  W is a linear layer's
+# [out, in] weight with out = L * 2 * nkv * 128 in all_kv's column order.
+
+@dataclass
+class ProjectWorkload:
+    name: str
+    num_ctx: int
+    hidden: int
+    num_layers: int
+    num_kv_heads: int
+    rotary_dim: int
+    block_size: int
+    num_blocks: int
+    fp8: bool
+    eps: float
+    states: np.ndarray              # uint16 bf16 bits [N, hidden]
+    hidden_norm_weight: np.ndarray  # uint16 bf16 bits [hidden]
+    kv_weight: np.ndarray           # uint16 bf16 bits [L * 2 * nkv * 128, hidden]
+    k_norm_weight: np.ndarray       # uint16 bf16 bits [L, 128]
+    positions: np.ndarray           # int64 [N]
+    slot_mapping: np.ndarray        # int64 [N]
+    cos_sin: np.ndarray             # uint16 bf16 bits [rows, R]
+    k_scales: np.ndarray            # float32 [L]
+    v_scales: np.ndarray            # float32 [L]
+    normalized: bool = False        # states are already the hidden_norm output
+
+    @property
+    def out_features(self) -> int:
+        return self.num_layers * 2 * self.num_kv_heads * HEAD_DIM
+
+    def write_workload(self, all_kv_bits: np.ndarray) -> Workload:
+        """The context write this projection feeds, with the given all_kv."""
+        return Workload(self.name + "_write", self.num_ctx, self.num_layers, self.num_kv_heads,
+                        self.rotary_dim, self.block_size, self.num_blocks, self.fp8, self.eps,
+                        np.ascontiguousarray(all_kv_bits.reshape(
+                            self.num_ctx, self.num_layers, 2, self.num_kv_heads, HEAD_DIM)),
+                        self.k_norm_weight, self.positions, self.slot_mapping, self.cos_sin,
+                        self.k_scales, self.v_scales)
+
+    def gemm_flops(self) -> int:
+        return 2 * self.num_ctx * self.hidden * self.out_features
+
+
+PROJECT_NAMES = ["project_tiny", "project_prefill_bf16", "project_prefill_fp8"]
+
+PROJECT_DESCRIPTIONS = [
+    "N=64 hidden=256 L=2 nkv=2 R=64 bs=16 8 blocks bf16 cache, ~10% padding",
+    "N=4096 (4 x 1024) hidden=6144 L=5 nkv=8 R=64 bs=64 512 blocks bf16 caches, 2% padding",
+    "N=4096 (4 x 1024) hidden=6144 L=5 nkv=8 R=64 bs=64 512 blocks fp8 e4m3 caches, 2% padding",
+]
+
+
+def _quantized(rng, shape, max_int, exp):
+    """Integers uniform in [-max_int, max_int] times 2^exp, as bf16 bits
+    (exact: max_int < 256)."""
+    k = rng.integers(-max_int, max_int + 1, size=shape).astype(np.float32)
+    return to_bf16_bits(k * np.float32(2.0 ** exp))
+
+
+def project_make(index: int, variant: int = 0) -> ProjectWorkload:
+    """Workload ``index`` (0..2, in the order of PROJECT_NAMES)."""
+    rng = np.random.default_rng(3000 + index + 7919 * variant)
+    if index == 0:
+        N, hidden, L, nkv, R, bs, nb, fp8, pad, rows = 64, 256, 2, 2, 64, 16, 8, False, 0.10, 4096
+    elif index in (1, 2):
+        N, hidden, L, nkv, R, bs, nb, fp8, pad, rows = 4096, 6144, 5, 8, 64, 64, 512, index == 2, 0.02, 4096
+    else:
+        raise ValueError("project workload index must be 0..2")
+    C = L * 2 * nkv * HEAD_DIM
+    states = _normal_bf16(rng, (N, hidden), 1.0)
+    hw = _normal_bf16(rng, (hidden,), 0.1)
+    W = _normal_bf16(rng, (C, hidden), 1.0 / np.sqrt(hidden))
+    kw = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+    if fp8:
+        ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+    else:
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+    if index == 0:
+        slots = rng.permutation(nb * bs)[:N].astype(np.int64)
+        positions = np.arange(N, dtype=np.int64)
+    else:
+        reqs, per = 4, 1024
+        bpr = per // bs
+        blocks = rng.permutation(nb)[:reqs * bpr].reshape(reqs, bpr)
+        j = np.arange(per, dtype=np.int64)
+        slots = np.concatenate([blocks[r][j // bs] * bs + j % bs for r in range(reqs)]).astype(np.int64)
+        positions = np.tile(np.arange(per, dtype=np.int64), reqs)
+    slots = _pad(rng, slots, int(round(pad * N)))
+    return ProjectWorkload(PROJECT_NAMES[index], N, hidden, L, nkv, R, bs, nb, fp8, 1e-6,
+                           states, hw, W, kw, positions, slots, rope_table(rows, R), ks, vs)
+
+
+def project_exact(num_ctx, hidden, num_layers, num_kv_heads, rotary_dim, block_size,
+                  num_blocks, fp8, seed, pad_fraction=0.1) -> ProjectWorkload:
+    """Normalized states and weights on coarse grids, z = k 2^-5 (|k| <= 63)
+    and W = m 2^-9 (|m| <= 31): every product is a multiple of 2^-14 below
+    0.12 and every partial sum of up to 8192 terms stays below 1024 = 2^24 *
+    2^-14, so fp32 accumulation in any order gives the exact sum."""
+    assert hidden <= 8192
+    rng = np.random.default_rng(seed)
+    N, L, nkv = num_ctx, num_layers, num_kv_heads
+    C = L * 2 * nkv * HEAD_DIM
+    z = _quantized(rng, (N, hidden), 63, -5)
+    W = _quantized(rng, (C, hidden), 31, -9)
+    kw = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+    if fp8:
+        ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+    else:
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+    slots = rng.permutation(num_blocks * block_size)[:N].astype(np.int64)
+    slots = _pad(rng, slots, int(round(pad_fraction * N)))
+    rows = N + 64
+    positions = rng.integers(0, rows, size=N).astype(np.int64)
+    return ProjectWorkload("project_exact", N, hidden, L, nkv, rotary_dim, block_size, num_blocks,
+                           fp8, 1e-6, z, np.zeros(hidden, np.uint16), W, kw, positions, slots,
+                           rope_table(rows, rotary_dim), ks, vs, normalized=True)
