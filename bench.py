@@ -343,6 +343,74 @@ def time_unfused(setup: UnfusedSetup, steps: int, warmup: int, stream):
     return start.elapsed_time(end) * 1e-3 / steps
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+class ProjectSetup:
+    """The step before the write at one workload: context states, hidden-norm
+    weight, the stacked K/V projection and the layers' caches."""
+
+    def __init__(self, index: int, dev):
+        wl = W.project_make(index)
+        self.wl = wl
+        layers = []
+        for l in range(wl.num_layers):
+            shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, 256)
+            if wl.fp8:
+                cache = torch.full(shape, 0xFF, dtype=torch.uint8, device=dev)
+            else:
+                cache = torch.full(shape, -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+            layers.append(AttnLayer(cache, torch.tensor([float(wl.k_scales[l])], device=dev),
+                                    torch.tensor([float(wl.v_scales[l])], device=dev),
+                                    "fp8" if wl.fp8 else "auto"))
+        self.layers = layers
+        self.writer = DSparkContextKVWriter(layers)
+        self.states = bf16_dev(wl.states, dev)
+        self.hw = bf16_dev(wl.hidden_norm_weight, dev)
+        self.W = bf16_dev(wl.kv_weight, dev)
+        self.kw = bf16_dev(wl.k_norm_weight, dev)
+        self.pos = torch.from_numpy(wl.positions).to(dev)
+        self.cs = bf16_dev(wl.cos_sin, dev)
+        self.slots = torch.from_numpy(wl.slot_mapping).to(dev)
+        self.z = torch.empty_like(self.states)
+        from speculative_decoding_draft_02_amd.project import hidden_norm
+        self._hidden_norm = hidden_norm
+
+    def norm(self):
+        self._hidden_norm(self.states, self.hw, self.wl.eps, out=self.z)
+
+    def project_write(self):
+        wl = self.wl
+        self.writer.project_write(self.z, self.W, self.kw, wl.eps, self.pos, self.cs,
+                                  wl.rotary_dim, self.slots)
+
+    def unfused(self):
+        """hidden norm, the projection as a library GEMM (torch's linear, on
+        hipBLASLt), all_kv stored, then the context write kernel."""
+        wl = self.wl
+        self.norm()
+        all_kv = torch.nn.functional.linear(self.z, self.W)
+        self.writer(all_kv.view(wl.num_ctx, wl.num_layers, 2, wl.num_kv_heads, 128), self.kw,
+                    wl.eps, self.pos, self.cs, wl.rotary_dim, self.slots)
+
+
+def time_calls(fn, steps: int, warmup: int, stream) -> float:
+    """Seconds per call of fn (a sequence of launches) over `steps` calls
+    bracketed by HIP events on the stream."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
 def small_copy_reference(nbytes_moved: float, n_bufs: int, stream, per_graph: int = 64,
                          replays: int = 16):
     """Graph-replayed device copies that read and write nbytes_moved / 2
@@ -449,7 +517,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all", "insert"] + W.NAMES)
+    ap.add_argument("--workload", default="all", choices=["all", "insert", "project"] + W.NAMES)
     ap.add_argument("--insert-sets", type=int, default=32,
                     help="draft blocks rotated in the insert's graph")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated in the timed loop")
@@ -554,6 +622,38 @@ def main():
         del setup
         torch.cuda.empty_cache()
 
+    if args.workload in ("all", "project"):
+        # the step before the write: hidden norm, then the projection on the
+        # matrix cores with the write fused into its epilogue
+        for index in (1, 2):
+            name = W.PROJECT_NAMES[index]
+            log("workload", name, "setup")
+            ps = ProjectSetup(index, dev)
+            steps = max(10, min(args.steps, 50))
+            t_norm = time_calls(ps.norm, steps, 3, stream)
+            t_pw = time_calls(ps.project_write, steps, 3, stream)
+            t_fused = time_calls(lambda: (ps.norm(), ps.project_write()), steps, 3, stream)
+            t_unfused = time_calls(ps.unfused, steps, 3, stream)
+            wl = ps.wl
+            flops = wl.gemm_flops()
+            norm_bytes = 2 * wl.num_ctx * wl.hidden * 2 + wl.hidden * 2
+            results[name] = {
+                "config": W.PROJECT_DESCRIPTIONS[index],
+                "hidden_norm_us": t_norm * 1e6,
+                "hidden_norm_GB_s": norm_bytes / t_norm / 1e9,
+                "project_write_us": t_pw * 1e6,
+                "project_write_TFLOP_s": flops / t_pw / 1e12,
+                "pct_of_bf16_mfma_peak": 100.0 * flops / t_pw / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                "pipeline_us": t_fused * 1e6,
+                "unfused_pipeline_us": t_unfused * 1e6,
+                "unfused_pipeline": "hidden norm, torch linear (hipBLASLt) writing all_kv, "
+                                    "context write kernel",
+                "speedup_of_fused": t_unfused / t_fused,
+                "gemm_flops": flops, "steps": steps}
+            log(name, json.dumps(results[name]))
+            del ps
+            torch.cuda.empty_cache()
+
     if args.workload in ("all", "insert"):
         # the draft block's fused QK-norm / RoPE / KV insert (448 draft rows)
         for index in (1, 2):
@@ -598,10 +698,12 @@ def main():
                            "algorithmic_bytes_per_launch": h["bytes_per_call"]}
     else:
         name = next(iter(results))
-        out.update({"value": results[name]["GB_s"],
-                    "ms_per_step": results[name].get("ms_per_step", results[name].get("us_per_call", 0) / 1e3)})
+        r0 = results[name]
+        out.update({"value": r0.get("GB_s", r0.get("project_write_TFLOP_s")),
+                    "ms_per_step": r0.get("ms_per_step", r0.get("us_per_call",
+                                                                r0.get("pipeline_us", 0)) / 1e3)})
         desc = (W.DESCRIPTIONS[W.NAMES.index(name)] if name in W.NAMES
-                else W.INSERT_DESCRIPTIONS[W.INSERT_NAMES.index(name)])
+                else results[name].get("config", ""))
         out["config"] = {"workload": name + ": " + desc}
         out["roofline"] = None
     out["workloads"] = results

@@ -1,0 +1,66 @@
+/*
+ * dspark_project.h - C ABI of the step before the DSpark context-KV write on
+ * MI355X (gfx950): the Gemma hidden norm of the context states and the
+ * token-major K/V projection, with the context write fused into the
+ * projection's epilogue.
+ *
+ * What is computed follows the vLLM API page
+ * "vllm.models.minimax_m3.common.dspark" (MiniMaxM3DSparkModel):
+ * _normalize_context_states applies the draft's Gemma hidden_norm
+ * (_gemma_rms_norm) to the target's context states,
+ * _project_context_kv_token_major multiplies them by the stacked K/V
+ * projection of every draft layer into all_kv [num_ctx, L, 2, nkv, 128], and
+ * precompute_and_store_context_kv hands all_kv to the fused context write
+ * (dspark_ctx_kv.h).  Here the write runs inside the projection kernel, so
+ * all_kv is never stored.
+ */
+#ifndef DSPARK_PROJECT_H
+#define DSPARK_PROJECT_H
+
+#include <stdint.h>
+
+#include "dspark_ctx_kv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Gemma RMSNorm of every row: out[r, i] = bf16( x[r, i] * rsqrt(mean_i
+ * x[r, i]^2 + eps) * (1 + weight[i]) ), the norm in fp32.  x and out are bf16
+ * [rows, dim] (they may be the same buffer), weight bf16 [dim]; all three
+ * 16-byte aligned; dim a positive multiple of 8.  One launch on `stream` (a
+ * hipStream_t, NULL = null stream), no allocation; rows == 0 returns DSPARK_OK
+ * without a launch.  Returns DSPARK_OK, DSPARK_E_ARG (reason in
+ * dspark_ctx_kv_last_error()) or DSPARK_E_HIP. */
+int dspark_hidden_norm(const void *x, int64_t rows, int32_t dim, const void *weight, float eps,
+                       void *out, void *stream);
+
+/* The projection all_kv = bf16(states @ kv_weight^T) with the context write
+ * of dspark_ctx_kv_writer_write applied to it in the same kernel:
+ *   states     bf16 [num_ctx, hidden], the hidden-norm output, contiguous,
+ *              16-byte aligned; hidden a positive multiple of 64
+ *   kv_weight  bf16 [num_layers * 2 * num_kv_heads * 128, hidden], a linear
+ *              layer's [out, in] weight whose output row is ordered as
+ *              all_kv's (layer, K/V, kv head, dim), 16-byte aligned
+ * and the remaining arguments exactly as for dspark_ctx_kv_writer_write
+ * (the writer's layers, kv heads, caches and scales; k_norm_weight, eps,
+ * positions, cos_sin_cache, rotary_dim, slot_mapping, and its
+ * preconditions).  The projection accumulates in fp32 on the matrix cores
+ * and rounds each all_kv value to bf16 before the write's norm and RoPE, as
+ * the unfused projection's bf16 output would be.  One kernel launch, no
+ * allocation, synchronisation or copy (graph-capturable).  num_ctx == 0
+ * returns DSPARK_OK without a launch.  Returns DSPARK_OK, DSPARK_E_ARG or
+ * DSPARK_E_HIP. */
+int dspark_ctx_kv_writer_project_write(dspark_ctx_kv_writer *w, const void *states,
+                                       int64_t num_ctx, int32_t hidden, const void *kv_weight,
+                                       int32_t num_layers, int32_t num_kv_heads,
+                                       const void *k_norm_weight, float eps,
+                                       const int64_t *positions, const void *cos_sin_cache,
+                                       int64_t cos_sin_rows, int32_t rotary_dim,
+                                       const int64_t *slot_mapping, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_PROJECT_H */

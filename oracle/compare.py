@@ -267,3 +267,77 @@ def compare_insert(dev_qkv, dev_cache, dev_q_fp8, oracle_result, num_heads: int,
         qflat = np.arange(df.size, dtype=np.int64).reshape(df.shape)
         parts["q_fp8"] = _grade(df, r.q_fp8, qflat, alt_map(2), ordinal_e4m3, False)
     return InsertReport(parts=parts, untouched_bad=untouched)
+
+
+# ------------------------------------- projection + write on general data ----
+#
+# With Gaussian data the device's fp32 accumulation of the projection is not
+# exact, so its bf16 all_kv may differ from the exactly rounded value.  The
+# acceptance is then an interval per stored element, derived from the
+# arithmetic and propagated through the write with interval arithmetic:
+#   * all_kv: |acc - exact| <= gamma_n * sum|z W| (n = hidden, any summation
+#     order, exact products; gamma_n = n u / (1 - n u), u = 2^-24), plus
+#     sum |W| |dz| over the hidden-norm near ties where the device may hold the
+#     other bf16 neighbour of z; bf16 rounding is monotone, so the device's
+#     value lies in [RNE(exact - b), RNE(exact + b)];
+#   * K: the norm's r over the interval box, x r (1 + w) over the corners,
+#     RoPE over the corners, each fp32 stage widened by 2^-19 relative (fp32
+#     evaluation and v_rsq_f32), then rounded to bf16 outward;
+#   * fp8: e4m3 of value / scale is monotone, so the interval maps through.
+
+_U = 2.0 ** -24
+_WIDEN = 2.0 ** -19
+
+
+def _rne_bf16(x64):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float64)).to(torch.float32)
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _widen(lo, hi):
+    return (lo - np.abs(lo) * _WIDEN - 1e-38, hi + np.abs(hi) * _WIDEN + 1e-38)
+
+
+def write_intervals(exact, abs_sum, dz_term, hidden, k_norm_weight, cos, sin, rotary_dim, kv,
+                    eps=1e-6):
+    """Bounds [lo, hi] (float64, bf16 values) of the stored values of one
+    all_kv row group.  exact, abs_sum, dz_term: [T, 128] for one (layer, kv,
+    head); k_norm_weight: [128] float; cos, sin: [T, R/2] float; kv 0 = K."""
+    n = float(hidden)
+    gamma = n * _U / (1.0 - n * _U)
+    b = gamma * (abs_sum + dz_term) + dz_term
+    xlo = _rne_bf16(exact - b)
+    xhi = _rne_bf16(exact + b)
+    if kv == 1:
+        return xlo, xhi
+    # the norm's r over the box: mean x^2 between the smallest and largest squares
+    sq_lo = np.where((xlo <= 0) & (xhi >= 0), 0.0, np.minimum(xlo * xlo, xhi * xhi))
+    sq_hi = np.maximum(xlo * xlo, xhi * xhi)
+    eps = float(np.float32(eps))
+    r_lo = 1.0 / np.sqrt(sq_hi.mean(axis=1, keepdims=True) + eps)
+    r_hi = 1.0 / np.sqrt(sq_lo.mean(axis=1, keepdims=True) + eps)
+    r_lo, r_hi = _widen(r_lo, r_hi)
+    g = 1.0 + k_norm_weight[None, :]
+    c = np.stack([xlo * r_lo * g, xlo * r_hi * g, xhi * r_lo * g, xhi * r_hi * g])
+    ylo, yhi = _widen(c.min(axis=0), c.max(axis=0))
+    ylo, yhi = _rne_bf16(ylo), _rne_bf16(yhi)
+    R = rotary_dim
+    h = R // 2
+    klo, khi = ylo.copy(), yhi.copy()
+    a_lo, a_hi = ylo[:, :h], yhi[:, :h]
+    p_lo, p_hi = ylo[:, h:R], yhi[:, h:R]
+
+    def prod(lo, hi, s):
+        v = np.stack([lo * s, hi * s])
+        return v.min(axis=0), v.max(axis=0)
+
+    ac_lo, ac_hi = prod(a_lo, a_hi, cos)
+    ps_lo, ps_hi = prod(p_lo, p_hi, sin)
+    pc_lo, pc_hi = prod(p_lo, p_hi, cos)
+    as_lo, as_hi = prod(a_lo, a_hi, sin)
+    f_lo, f_hi = _widen(ac_lo - ps_hi, ac_hi - ps_lo)     # first half: a c - p s
+    s_lo, s_hi = _widen(pc_lo + as_lo, pc_hi + as_hi)     # second half: p c + a s
+    klo[:, :h], khi[:, :h] = _rne_bf16(f_lo), _rne_bf16(f_hi)
+    klo[:, h:R], khi[:, h:R] = _rne_bf16(s_lo), _rne_bf16(s_hi)
+    return klo, khi

@@ -1,5 +1,5 @@
-"""ctypes binding of libdspark_ctx_kv.so (include/dspark_ctx_kv.h and
-include/dspark_qknorm_insert.h).
+"""ctypes binding of libdspark_ctx_kv.so (include/dspark_ctx_kv.h,
+include/dspark_qknorm_insert.h and include/dspark_project.h).
 
 Argument marshalling only: every function here has the name and argument
 order of the C entry point it calls, takes device pointers as Python ints,
@@ -37,6 +37,9 @@ SIGNATURES = {
     "dspark_ctx_kv_writer_destroy": ([_P], None),
     "dspark_rotary_dims_supported": ([_I32, _I32], ctypes.c_int),
     "dspark_ctx_kv_last_error": ([], ctypes.c_char_p),
+    "dspark_hidden_norm": ([_P, _I64, _I32, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_project_write": ([_P, _P, _I64, _I32, _P, _I32, _I32, _P, ctypes.c_float,
+                                            _P, _P, _I64, _I32, _P, _P], ctypes.c_int),
     "dspark_qknorm_rope_kv_insert": ([_P, _I64, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                       ctypes.c_float, _P, _P, _I64, _I32, _I32, _P, _P, _P,
                                       ctypes.c_float, _P], ctypes.c_int),
@@ -126,3 +129,15 @@ def dspark_qknorm_rope_kv_insert(qkv, num_tokens, q_norm_weight, k_norm_weight, 
         qkv, num_tokens, q_norm_weight, k_norm_weight, cos_sin_cache, cos_sin_rows, positions,
         num_heads, num_kv_heads, rotary_dim, eps, slot_mapping, kv_cache, num_blocks, block_size,
         kv_cache_dtype, k_scale, v_scale, q_fp8_out, q_fp8_scale, stream)
+
+
+def dspark_hidden_norm(x, rows, dim, weight, eps, out, stream) -> int:
+    return load().dspark_hidden_norm(x, rows, dim, weight, eps, out, stream)
+
+
+def dspark_ctx_kv_writer_project_write(writer, states, num_ctx, hidden, kv_weight, num_layers,
+                                       num_kv_heads, k_norm_weight, eps, positions, cos_sin_cache,
+                                       cos_sin_rows, rotary_dim, slot_mapping, stream) -> int:
+    return load().dspark_ctx_kv_writer_project_write(
+        writer, states, num_ctx, hidden, kv_weight, num_layers, num_kv_heads, k_norm_weight, eps,
+        positions, cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspark_ctx_kv.so")
-SOURCES = ["ctx_kv_kernel.hip", "ctx_kv_writer.cpp", "qknorm_insert_kernel.hip", "qknorm_insert.cpp"]
+SOURCES = ["ctx_kv_kernel.hip", "ctx_kv_writer.cpp", "qknorm_insert_kernel.hip", "qknorm_insert.cpp",
+           "project_kernel.hip", "project.cpp"]
 ARCH = "gfx950"
 
 

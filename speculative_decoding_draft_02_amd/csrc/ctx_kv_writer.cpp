@@ -19,21 +19,9 @@
 
 #include "ctx_kv_args.h"
 #include "qknorm_insert_args.h"
+#include "writer_state.h"
 #include "dspark_ctx_kv.h"
 
-struct dspark_ctx_kv_writer {
-    int32_t num_layers;
-    int32_t num_kv_heads;
-    int32_t block_size;
-    int32_t bs_log2;
-    int64_t num_blocks;
-    int32_t kv_cache_dtype;
-    void *cache0;
-    const float *scale0;
-    int64_t cache_off[DSPARK_MAX_LAYERS];
-    int64_t kscale_off[DSPARK_MAX_LAYERS];
-    int64_t vscale_off[DSPARK_MAX_LAYERS];
-};
 
 namespace {
 thread_local std::string g_last_error;

@@ -212,6 +212,49 @@ class DSparkContextKVWriter:
         if st != _lib.OK:
             raise RuntimeError("DSpark context-KV write failed: " + _lib.dspark_ctx_kv_last_error())
 
+    def project_write(self, states: torch.Tensor, kv_weight: torch.Tensor,
+                      k_norm_weight: torch.Tensor, eps: float, positions: torch.Tensor,
+                      cos_sin_cache: torch.Tensor, rotary_dim: int,
+                      slot_mapping: torch.Tensor) -> None:
+        """The projection all_kv = states @ kv_weight.T with this write fused
+        into its epilogue (all_kv is never stored).  states: bf16
+        [num_ctx, hidden], the hidden-norm output; kv_weight: bf16
+        [L * 2 * nkv * 128, hidden] ([out, in], rows in all_kv's order);
+        slot_mapping: one int64 [num_ctx] tensor shared by every layer."""
+        L, nkv = self._num_layers, self._num_kv_heads
+        dev = self._layers[0].kv_cache.device
+        if states.dim() != 2:
+            raise ValueError("states must be [num_ctx, hidden]")
+        num_ctx, hidden = states.shape
+        for name, t, dt in (("states", states, torch.bfloat16),
+                            ("kv_weight", kv_weight, torch.bfloat16),
+                            ("k_norm_weight", k_norm_weight, torch.bfloat16),
+                            ("positions", positions, torch.int64),
+                            ("cos_sin_cache", cos_sin_cache, torch.bfloat16),
+                            ("slot_mapping", slot_mapping, torch.int64)):
+            if t.dtype != dt or t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+        if tuple(kv_weight.shape) != (L * 2 * nkv * HEAD_DIM, hidden):
+            raise ValueError(f"kv_weight has shape {tuple(kv_weight.shape)}, "
+                             f"expected {(L * 2 * nkv * HEAD_DIM, hidden)}")
+        if tuple(k_norm_weight.shape) != (L, HEAD_DIM):
+            raise ValueError(f"k_norm_weight has shape {tuple(k_norm_weight.shape)}")
+        if positions.shape != (num_ctx,) or slot_mapping.shape != (num_ctx,):
+            raise ValueError("positions and slot_mapping must have shape (num_ctx,)")
+        if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != rotary_dim:
+            raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}")
+        if num_ctx == 0:
+            return
+        self._ensure_tables()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = _lib.dspark_ctx_kv_writer_project_write(
+            self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(), L, nkv,
+            k_norm_weight.data_ptr(), float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
+            cos_sin_cache.shape[0], int(rotary_dim), slot_mapping.data_ptr(), stream)
+        if st != _lib.OK:
+            raise RuntimeError("DSpark projection + context-KV write failed: "
+                               + _lib.dspark_ctx_kv_last_error())
+
     def close(self) -> None:
         if self._handle is not None:
             _lib.dspark_ctx_kv_writer_destroy(self._handle)

@@ -12,7 +12,8 @@ import pytest
 from speculative_decoding_draft_02_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("dspark_ctx_kv.h", "dspark_qknorm_insert.h")]
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in ("dspark_ctx_kv.h", "dspark_qknorm_insert.h", "dspark_project.h")]
 
 
 @pytest.fixture(scope="module")
@@ -279,3 +280,47 @@ def test_qknorm_insert_argument_checks(lib):
     # no q fp8 output: its scale is not looked at
     assert call(num_tokens=0, q_fp8_out=None, q_fp8_scale=0.0) == _lib.OK
     assert call(num_tokens=0) == _lib.OK
+
+
+def test_hidden_norm_and_project_write_argument_checks(lib):
+    fake = BASE + 0x100000
+    E = _lib.dspark_ctx_kv_last_error
+    hn = _lib.dspark_hidden_norm
+    assert hn(fake, -1, 512, fake, 1e-6, fake, None) == _lib.E_ARG and "negative" in E()
+    assert hn(fake, 4, 500, fake, 1e-6, fake, None) == _lib.E_ARG and "multiple of 8" in E()
+    assert hn(fake, 4, 0, fake, 1e-6, fake, None) == _lib.E_ARG
+    assert hn(0, 4, 512, fake, 1e-6, fake, None) == _lib.E_ARG and "NULL" in E()
+    assert hn(fake + 8, 4, 512, fake, 1e-6, fake, None) == _lib.E_ARG and "16-byte" in E()
+    assert hn(fake, 1 << 31, 512, fake, 1e-6, fake, None) == _lib.E_ARG
+    assert hn(fake, 0, 512, fake, 1e-6, fake, None) == _lib.OK        # no launch
+
+    st, w = _lib.dspark_ctx_kv_writer_create(*_layout(L=2, nkv=2))
+    assert st == _lib.OK
+
+    def pw(**kw):
+        a = dict(writer=w, states=fake, num_ctx=300, hidden=512, kv_weight=fake, num_layers=2,
+                 num_kv_heads=2, k_norm_weight=fake, eps=1e-6, positions=fake,
+                 cos_sin_cache=fake, cos_sin_rows=4096, rotary_dim=64, slot_mapping=fake,
+                 stream=None)
+        a.update(kw)
+        return _lib.dspark_ctx_kv_writer_project_write(*a.values())
+
+    for kw, reason in [
+        (dict(writer=None), "writer is NULL"),
+        (dict(num_layers=3), "built for 2 and 2"),
+        (dict(num_kv_heads=4), "built for 2 and 2"),
+        (dict(rotary_dim=48), "rotary_dim 48"),
+        (dict(hidden=96), "multiple of 64"),
+        (dict(hidden=0), "multiple of 64"),
+        (dict(num_ctx=-1), "negative"),
+        (dict(num_ctx=1 << 31), "exceeds"),
+        (dict(kv_weight=0), "NULL"),
+        (dict(slot_mapping=0), "NULL"),
+        (dict(states=fake + 8), "16-byte aligned"),
+        (dict(positions=fake + 4), "8-byte aligned"),
+        (dict(cos_sin_rows=0), "no rows"),
+    ]:
+        assert pw(**kw) == _lib.E_ARG, kw
+        assert reason in E(), (kw, E())
+    assert pw(num_ctx=0) == _lib.OK                                    # no launch
+    _lib.dspark_ctx_kv_writer_destroy(w)

@@ -1,0 +1,266 @@
+"""Parity of the step before the write on MI355X (through the C ABI): the
+Gemma hidden norm, and the token-major K/V projection on the matrix cores
+with the context write fused into its epilogue.
+
+* Hidden norm: bit-exact with the oracle except at recorded near ties, where
+  the other bf16 neighbour is also correct.
+* Projection + write on exactly-summable grids (every fp32 partial sum is
+  exact, so the projection has one correct result): the caches meet the
+  context write's acceptance rule against the oracle's write of the oracle's
+  projection (V bit-exact in bf16 caches).
+* The full-size pipeline on Gaussian data: every stored value of sampled
+  tokens lies in the interval derived from the fp32 accumulation bound
+  (oracle/compare.py, write_intervals), at least 99% are bit-exact with the
+  oracle, and every unwritten cache row is untouched."""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare as C
+from speculative_decoding_draft_02_amd import workloads as W
+from speculative_decoding_draft_02_amd.project import hidden_norm, precompute_and_store_context_kv
+from speculative_decoding_draft_02_amd.writer import AttnLayer, DSparkContextKVWriter
+from tests._util import bits_to_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    arch = torch.cuda.get_device_properties(0).gcnArchName
+    assert arch.startswith("gfx950"), arch
+
+
+def _bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def _codes(t):
+    return t.cpu().numpy() if t.dtype == torch.uint8 else t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _layers(wl):
+    out = []
+    for l in range(wl.num_layers):
+        shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, 256)
+        if wl.fp8:
+            cache = torch.full(shape, W.SENTINEL_FP8, dtype=torch.uint8, device=DEV)
+        else:
+            cache = torch.full(shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        ks = torch.tensor([float(wl.k_scales[l])], dtype=torch.float32, device=DEV)
+        vs = torch.tensor([float(wl.v_scales[l])], dtype=torch.float32, device=DEV)
+        out.append(AttnLayer(cache, ks, vs, "fp8" if wl.fp8 else "auto"))
+    return out
+
+
+@pytest.mark.parametrize("rows,dim", [(1, 8), (5, 256), (300, 1000), (64, 6144), (7, 12288)])
+def test_hidden_norm_parity(oracle_lib, rows, dim):
+    print("case hidden_norm", rows, dim, flush=True)
+    rng = np.random.default_rng(rows * 7 + dim)
+    x = W._normal_bf16(rng, (rows, dim), 1.0)
+    w = W._normal_bf16(rng, (dim,), 0.1)
+    got = _codes(hidden_norm(_bf16(x), _bf16(w), 1e-6))
+    ref, idx, other = oracle_lib.gemma_rms_norm(x, w, 1e-6)
+    diff = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
+    alt = dict(zip(idx.tolist(), other.tolist()))
+    bad = [int(i) for i in diff if alt.get(int(i)) != int(got.reshape(-1)[i])]
+    print("hidden_norm", rows, dim, "differences", diff.size, "near ties", idx.size, flush=True)
+    assert not bad, bad[:10]
+
+
+def test_hidden_norm_in_place(oracle_lib):
+    rng = np.random.default_rng(3)
+    x = W._normal_bf16(rng, (33, 512), 2.0)
+    w = W._normal_bf16(rng, (512,), 0.1)
+    t = _bf16(x)
+    hidden_norm(t, _bf16(w), 1e-6, out=t)
+    ref, idx, other = oracle_lib.gemma_rms_norm(x, w, 1e-6)
+    got = _codes(t)
+    diff = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
+    alt = dict(zip(idx.tolist(), other.tolist()))
+    assert all(alt.get(int(i)) == int(got.reshape(-1)[i]) for i in diff)
+
+
+EXACT_SWEEP = [
+    # (N, hidden, L, nkv, R, bs, blocks, fp8, pad)
+    (1, 64, 1, 1, 16, 1, 2, False, 0.0),
+    (300, 256, 2, 2, 64, 16, 32, False, 0.1),
+    (300, 512, 1, 3, 32, 4, 128, True, 0.2),
+    (513, 192, 2, 1, 16, 2, 300, True, 0.0),
+    (256, 1024, 3, 2, 64, 64, 8, False, 0.5),
+    (1000, 128, 1, 8, 32, 128, 8, True, 0.05),
+    (700, 2048, 2, 4, 64, 16, 64, False, 0.02),
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_SWEEP,
+                         ids=lambda s: "N%d-h%d-L%d-kv%d-R%d-bs%d-%s" % (s[0], s[1], s[2], s[3], s[4], s[5],
+                                                                      "fp8" if s[7] else "bf16"))
+def test_project_write_exact_grids(oracle_lib, shape):
+    N, hidden, L, nkv, R, bs, nb, fp8, pad = shape
+    print("case project exact", shape, flush=True)
+    wl = W.project_exact(N, hidden, L, nkv, R, bs, nb, fp8, seed=N + hidden, pad_fraction=pad)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    writer.project_write(_bf16(wl.states), _bf16(wl.kv_weight), _bf16(wl.k_norm_weight), wl.eps,
+                         torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), R,
+                         torch.from_numpy(wl.slot_mapping).to(DEV))
+    torch.cuda.synchronize()
+    got = [_codes(a.kv_cache) for a in layers]
+    all_kv = oracle_lib.kv_project(wl.states, wl.kv_weight)
+    ww = wl.write_workload(all_kv)
+    ref = oracle_lib.ctx_kv_write(ww.all_kv, ww.k_norm_weight, ww.eps, ww.positions, ww.cos_sin, R,
+                                  ww.slot_mapping, ww.new_host_caches(), fp8, ww.k_scales,
+                                  ww.v_scales)
+    rep = C.compare(got, ref, ww.slot_mapping, fp8, ww.sentinel)
+    tot = rep.totals()
+    print("project exact", shape, json.dumps(tot), flush=True)
+    assert rep.failures == 0, tot
+    if not fp8:
+        assert tot["v"]["exact"] == tot["v"]["n"]
+    writer.close()
+
+
+def _sample_tokens(wl, count, seed):
+    valid = np.flatnonzero(wl.slot_mapping >= 0)
+    rng = np.random.default_rng(seed)
+    pick = np.sort(rng.choice(valid, size=min(count, valid.size), replace=False))
+    # always include the first and last valid tokens (tile edges)
+    return np.unique(np.concatenate([pick, valid[:1], valid[-1:]]))
+
+
+@pytest.mark.parametrize("index", [1, 2], ids=W.PROJECT_NAMES[1:])
+def test_project_pipeline_full_size(oracle_lib, index):
+    """hidden norm + fused projection/write at the full prefill shape
+    (4096 tokens, hidden 6144, 5 layers x 8 kv heads), Gaussian data."""
+    wl = W.project_make(index)
+    print("case project pipeline", wl.name, flush=True)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    states = _bf16(wl.states)
+    z_dev = torch.empty_like(states)
+    precompute_and_store_context_kv(writer, states, _bf16(wl.hidden_norm_weight), wl.eps,
+                                    _bf16(wl.kv_weight), _bf16(wl.k_norm_weight),
+                                    torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin),
+                                    wl.rotary_dim, torch.from_numpy(wl.slot_mapping).to(DEV),
+                                    workspace=z_dev)
+    torch.cuda.synchronize()
+
+    # 1. the hidden norm on every row
+    z_ref, idx, other = oracle_lib.gemma_rms_norm(wl.states, wl.hidden_norm_weight, wl.eps)
+    z_got = _codes(z_dev)
+    diff = np.flatnonzero(z_got.reshape(-1) != z_ref.reshape(-1))
+    alt = dict(zip(idx.tolist(), other.tolist()))
+    assert all(alt.get(int(i)) == int(z_got.reshape(-1)[i]) for i in diff)
+
+    # 2. untouched rows, on the device
+    bs, nkv, L = wl.block_size, wl.num_kv_heads, wl.num_layers
+    rows = C.written_rows(wl.slot_mapping, nkv, bs)
+    mask = torch.ones(wl.num_blocks * nkv * bs, dtype=torch.bool, device=DEV)
+    mask[torch.from_numpy(rows).to(DEV)] = False
+    for a in layers:
+        flat = a.kv_cache.view(torch.uint8 if wl.fp8 else torch.int16).view(-1, 256)
+        sentinel = W.SENTINEL_FP8 if wl.fp8 else -1
+        assert int((flat[mask] != sentinel).sum()) == 0
+
+    # 3. sampled tokens: intervals from the accumulation bound, and bit-exactness
+    toks = _sample_tokens(wl, 40, seed=index)
+    zs = z_ref[toks]
+    codes, ex, ab = oracle_lib.kv_project(zs, wl.kv_weight, want_sums=True)
+    # near-tie term: sum |W| |dz| over this token's hidden-norm near ties
+    dz = np.zeros((toks.size, wl.hidden))
+    pos_in = {int(t): i for i, t in enumerate(toks)}
+    for k, o in zip(idx.tolist(), other.tolist()):
+        r, col = divmod(k, wl.hidden)
+        if r in pos_in:
+            i = pos_in[r]
+            dz[i, col] = abs(float(bits_to_f32(np.array([o]))[0]) -
+                             float(bits_to_f32(z_ref[r:r + 1, col])[0]))
+    dz_term = dz @ np.abs(bits_to_f32(wl.kv_weight).astype(np.float64)).T      # [T, C]
+    sub = W.Workload("sampled", toks.size, L, nkv, wl.rotary_dim, bs, wl.num_blocks, wl.fp8,
+                     wl.eps, np.ascontiguousarray(codes.reshape(toks.size, L, 2, nkv, 128)),
+                     wl.k_norm_weight, wl.positions[toks], wl.slot_mapping[toks], wl.cos_sin,
+                     wl.k_scales, wl.v_scales)
+    ref = oracle_lib.ctx_kv_write(sub.all_kv, sub.k_norm_weight, sub.eps, sub.positions,
+                                  sub.cos_sin, sub.rotary_dim, sub.slot_mapping,
+                                  sub.new_host_caches(), wl.fp8, sub.k_scales, sub.v_scales)
+    got = [_codes(a.kv_cache) for a in layers]
+    R = wl.rotary_dim
+    cs = bits_to_f32(wl.cos_sin[wl.positions[toks]]).astype(np.float64)
+    cos, sin = cs[:, :R // 2], cs[:, R // 2:]
+    blk, off = wl.slot_mapping[toks] // bs, wl.slot_mapping[toks] % bs
+    n_exact = n_all = 0
+    widths = []
+    for l in range(L):
+        kw = bits_to_f32(wl.k_norm_weight[l]).astype(np.float64)
+        for kv in (0, 1):
+            for h in range(nkv):
+                c0 = ((l * 2 + kv) * nkv + h) * 128
+                lo, hi = C.write_intervals(ex[:, c0:c0 + 128], ab[:, c0:c0 + 128],
+                                           dz_term[:, c0:c0 + 128], wl.hidden, kw, cos, sin, R, kv,
+                                           wl.eps)
+                crow = ((blk * nkv + h) * bs + off)
+                dev = got[l].reshape(-1, 256)[crow, kv * 128:(kv + 1) * 128]
+                orc = ref.caches[l].reshape(-1, 256)[crow, kv * 128:(kv + 1) * 128]
+                n_exact += int(np.count_nonzero(dev == orc))
+                n_all += dev.size
+                if wl.fp8:
+                    s = float(wl.k_scales[l] if kv == 0 else wl.v_scales[l])
+                    lo_c = C.ordinal_e4m3(oracle_lib_e4m3(lo / s))
+                    hi_c = C.ordinal_e4m3(oracle_lib_e4m3(hi / s))
+                    d = C.ordinal_e4m3(dev)
+                else:
+                    lo_c = C.ordinal_bf16(W.to_bf16_bits(lo))
+                    hi_c = C.ordinal_bf16(W.to_bf16_bits(hi))
+                    d = C.ordinal_bf16(dev)
+                widths.append(float(np.mean(hi_c - lo_c)))
+                out = (d < lo_c) | (d > hi_c)
+                assert not out.any(), (l, kv, h, int(out.sum()))
+    print("project pipeline", wl.name, "sampled", toks.size, "tokens; bit-exact %.5f" % (n_exact / n_all),
+          "mean interval width %.2f codes" % np.mean(widths), flush=True)
+    assert n_exact >= 0.99 * n_all
+    writer.close()
+
+
+def oracle_lib_e4m3(v):
+    """e4m3 codes of fp32 values with saturation (torch's conversion of the
+    clamped value, which the codec pins tie to the OCP definition)."""
+    t = torch.from_numpy(np.asarray(v, np.float64)).to(torch.float32).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_project_write_graph_capture(oracle_lib):
+    """The fused projection/write captured once and replayed: every replay
+    writes the oracle's result (the caches are refilled between replays)."""
+    wl = W.project_exact(300, 256, 2, 2, 32, 16, 32, True, seed=5)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    args = (_bf16(wl.states), _bf16(wl.kv_weight), _bf16(wl.k_norm_weight), wl.eps,
+            torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), wl.rotary_dim,
+            torch.from_numpy(wl.slot_mapping).to(DEV))
+    writer.project_write(*args)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            writer.project_write(*args)
+    all_kv = oracle_lib.kv_project(wl.states, wl.kv_weight)
+    ww = wl.write_workload(all_kv)
+    ref = oracle_lib.ctx_kv_write(ww.all_kv, ww.k_norm_weight, ww.eps, ww.positions, ww.cos_sin,
+                                  ww.rotary_dim, ww.slot_mapping, ww.new_host_caches(), True,
+                                  ww.k_scales, ww.v_scales)
+    for rep in range(3):
+        for a in layers:
+            a.kv_cache.fill_(W.SENTINEL_FP8)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [_codes(a.kv_cache) for a in layers]
+        assert C.compare(got, ref, ww.slot_mapping, True, ww.sentinel).failures == 0, rep
+    writer.close()
