@@ -170,6 +170,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) xs[s4] = (2 * s4 + hi) ^ sw;
 
+    // the epilogue's per-token inputs, requested now so that their latency
+    // hides behind the main loop: the position of token row tid (for the
+    // cos/sin staging) and the slot of this wave's store row wrow + lane
+    static_assert(32 * TI == 64, "one store row of the wave band per lane");
+    int64_t my_pos = 0;
+    if (tid < T::kBM) {
+        int64_t t = m0 + tid;
+        if (t >= a.num_ctx) t = a.num_ctx - 1;
+        my_pos = a.positions[t];
+    }
+    const int64_t my_slot = (m0 + wrow + lane < a.num_ctx) ? a.slots[m0 + wrow + lane] : -1;
+
     f32x16 acc[TI][4];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -181,7 +193,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     // set and slice kt + 2 is requested into the other; slice kt + 1 goes to
     // LDS after the MFMAs (its stage was last read before the previous
     // barrier).  The loop is unrolled by two so that both sets are named
-    // statically and stay in registers.
+    // statically and stay in registers.  A wave raises its issue priority
+    // while it runs its MFMAs, so that the other wave of its SIMD issues its
+    // loads and LDS traffic in the gaps rather than competing for the
+    // matrix core.
     constexpr int kP = T::kPA + T::kPB;
     u32x4 ra[kP], rb[kP];
     const int nk = a.hidden / kPK;
@@ -206,6 +221,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     do {                                                                                 \
         const int cur_ = ((kt) & 1) * T::kStage;                                         \
         if ((kt) + 2 < nk) DSPARK_FETCH(spare, (kt) + 2);                                \
+        __builtin_amdgcn_s_setprio(1);                                                   \
         _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                  \
             bf16x8 af[TI], bfr[4];                                                       \
             _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
@@ -217,6 +233,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                     acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                 \
                         bfr[n], af[i], acc[i][n], 0, 0, 0);                              \
         }                                                                                \
+        __builtin_amdgcn_s_setprio(0);                                                   \
         if ((kt) + 1 < nk) DSPARK_PUT(next, T::kStage - cur_);                           \
         __syncthreads();                                                                 \
     } while (0)
@@ -236,6 +253,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
         for (int kt = 0; kt < nk; ++kt) {
             const int cur_ = (kt & 1) * T::kStage;
             if (kt + 1 < nk) DSPARK_FETCH(ra, kt + 1);
+            __builtin_amdgcn_s_setprio(1);
             _Pragma("unroll") for (int s = 0; s < 4; ++s) {
                 bf16x8 af[TI], bfr[4];
                 _Pragma("unroll") for (int i = 0; i < TI; ++i)
@@ -247,6 +265,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                         acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[n], af[i], acc[i][n],
                                                                             0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
             if (kt + 1 < nk) DSPARK_PUT(ra, T::kStage - cur_);
             __syncthreads();
         }
@@ -262,12 +281,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     const int kv = (head / a.nkv) & 1;
     const int h = head % a.nkv;
     uint16_t *cs_lds = reinterpret_cast<uint16_t *>(lds + T::kCsOff);   // [kBM][R]
-    for (int r = tid; r < T::kBM; r += T::kThreads) {
-        int64_t t = m0 + r;
-        if (t >= a.num_ctx) t = a.num_ctx - 1;
-        const int64_t pos = a.positions[t];
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.cos_sin + pos * R);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(cs_lds + r * R);
+    static_assert(T::kThreads >= T::kBM, "one staging thread per token row");
+    if (tid < T::kBM) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.cos_sin + my_pos * R);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(cs_lds + tid * R);
 #pragma unroll
         for (int q = 0; q < R / 8; ++q) dst[q] = src[q];
     }
@@ -376,9 +393,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
 #pragma unroll 4
     for (int it = 0; it < 8 * TI; ++it) {
         const int rho = wrow + 4 * it + q4;
-        const int64_t t = m0 + rho;
-        if (t >= a.num_ctx) continue;
-        const int64_t slot = a.slots[t];
+        const int64_t slot = __shfl(my_slot, 4 * it + q4);   // < 0: padding or past num_ctx
         if (slot < 0) continue;
         const int64_t base = a.cache_off[layer] +
                              ((((slot >> a.bs_log2) * a.nkv + h) << a.bs_log2) + (slot & bmask)) *
