@@ -629,11 +629,20 @@ def main():
             name = W.PROJECT_NAMES[index]
             log("workload", name, "setup")
             ps = ProjectSetup(index, dev)
-            steps = max(10, min(args.steps, 50))
-            t_norm = time_calls(ps.norm, steps, 3, stream)
-            t_pw = time_calls(ps.project_write, steps, 3, stream)
-            t_fused = time_calls(lambda: (ps.norm(), ps.project_write()), steps, 3, stream)
-            t_unfused = time_calls(ps.unfused, steps, 3, stream)
+            # the clock settles over the first calls: warm both paths, then
+            # alternate rounds of each and take the medians
+            steps = max(10, min(args.steps, 20))
+            for fn in (ps.norm, ps.project_write, ps.unfused):
+                time_calls(fn, 10, 0, stream)
+            rounds = {"norm": [], "pw": [], "fused": [], "unfused": []}
+            for _ in range(5):
+                rounds["norm"].append(time_calls(ps.norm, steps, 0, stream))
+                rounds["pw"].append(time_calls(ps.project_write, steps, 0, stream))
+                rounds["fused"].append(time_calls(lambda: (ps.norm(), ps.project_write()),
+                                                  steps, 0, stream))
+                rounds["unfused"].append(time_calls(ps.unfused, steps, 0, stream))
+            t_norm, t_pw, t_fused, t_unfused = (float(np.median(rounds[k]))
+                                                for k in ("norm", "pw", "fused", "unfused"))
             wl = ps.wl
             flops = wl.gemm_flops()
             norm_bytes = 2 * wl.num_ctx * wl.hidden * 2 + wl.hidden * 2
@@ -649,7 +658,9 @@ def main():
                 "unfused_pipeline": "hidden norm, torch linear (hipBLASLt) writing all_kv, "
                                     "context write kernel",
                 "speedup_of_fused": t_unfused / t_fused,
-                "gemm_flops": flops, "steps": steps}
+                "gemm_flops": flops,
+                "timing": "medians of 5 alternating rounds of %d calls each, after 10 "
+                          "warm-up calls per path" % steps}
             log(name, json.dumps(results[name]))
             del ps
             torch.cuda.empty_cache()

@@ -280,13 +280,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     const int layer = head / (2 * a.nkv);
     const int kv = (head / a.nkv) & 1;
     const int h = head % a.nkv;
-    uint16_t *cs_lds = reinterpret_cast<uint16_t *>(lds + T::kCsOff);   // [kBM][R]
+    // the tile's [cos | sin] rows, [kBM][R]; row r's 16-byte chunk c sits at
+    // c ^ (r % (R / 8)) so that lanes reading one chunk of consecutive rows
+    // spread over the banks
+    constexpr int kCsMask = R / 8 - 1;
+    uint16_t *cs_lds = reinterpret_cast<uint16_t *>(lds + T::kCsOff);
     static_assert(T::kThreads >= T::kBM, "one staging thread per token row");
     if (tid < T::kBM) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.cos_sin + my_pos * R);
         u32x4 *dst = reinterpret_cast<u32x4 *>(cs_lds + tid * R);
 #pragma unroll
-        for (int q = 0; q < R / 8; ++q) dst[q] = src[q];
+        for (int q = 0; q < R / 8; ++q) dst[q ^ (tid & kCsMask)] = src[q];
     }
     __syncthreads();
 
@@ -344,8 +348,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
             constexpr int kQ = (R / 2) / 8;            // 8-column groups in the first half
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
-                const uint2 cw = *reinterpret_cast<const uint2 *>(cs + 8 * q + 4 * hi);
-                const uint2 sw2 = *reinterpret_cast<const uint2 *>(cs + R / 2 + 8 * q + 4 * hi);
+                const int cq = (q ^ (rho & kCsMask)) * 8 + 4 * hi;
+                const int sq = ((kQ + q) ^ (rho & kCsMask)) * 8 + 4 * hi;
+                const uint2 cw = *reinterpret_cast<const uint2 *>(cs + cq);
+                const uint2 sw2 = *reinterpret_cast<const uint2 *>(cs + sq);
                 const float c4[4] = {bf16_lo(cw.x), bf16_hi(cw.x), bf16_lo(cw.y), bf16_hi(cw.y)};
                 const float s4[4] = {bf16_lo(sw2.x), bf16_hi(sw2.x), bf16_lo(sw2.y), bf16_hi(sw2.y)};
 #pragma unroll
@@ -361,12 +367,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
         }
         // the finished values of this token into the head's row-major
         // [kBM][128] tile over the operand stages (every wave is past its
-        // last operand read): runs of 4 columns, 8 (bf16) or 4 (e4m3) bytes
+        // last operand read): runs of 4 columns, 8 (bf16) or 4 (e4m3) bytes.
+        // Row rho's 8-column units are permuted by unit ^ (rho % 16), so the
+        // 32 lanes writing one unit of 32 consecutive rows hit 16 bank groups.
 #pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = 32 * n + 8 * q + 4 * hi;
+                const int col = ((4 * n + q) ^ (rho & 15)) * 8 + 4 * hi;
                 const float *v = &y[n][4 * q];
                 if constexpr (!kFp8) {
                     uint2 *dst = reinterpret_cast<uint2 *>(
@@ -399,12 +407,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                              ((((slot >> a.bs_log2) * a.nkv + h) << a.bs_log2) + (slot & bmask)) *
                                  (2 * DSPARK_HEAD_DIM) +
                              kv * DSPARK_HEAD_DIM + c16 * 8;
+        const int unit = c16 ^ (rho & 15);                   // the row's permuted 8-column unit
         if constexpr (!kFp8) {
-            const u32x4 v = lds[(wn * T::kBM + rho) * 16 + c16];
+            const u32x4 v = lds[(wn * T::kBM + rho) * 16 + unit];
             store_row16(static_cast<uint16_t *>(a.cache0) + base, make_uint4(v.x, v.y, v.z, v.w));
         } else {
             store_row8(static_cast<uint8_t *>(a.cache0) + base,
-                       reinterpret_cast<const uint2 *>(lds)[(wn * T::kBM + rho) * 16 + c16]);
+                       reinterpret_cast<const uint2 *>(lds)[(wn * T::kBM + rho) * 16 + unit]);
         }
     }
 }
