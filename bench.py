@@ -42,6 +42,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["speculative_decoding_draft_02_amd/csrc/ctx_kv_kernel.hip",
                   "speculative_decoding_draft_02_amd/csrc/ctx_kv_writer.cpp",
                   "speculative_decoding_draft_02_amd/csrc/ctx_kv_args.h",
+                  "speculative_decoding_draft_02_amd/csrc/writer_state.h",
                   "speculative_decoding_draft_02_amd/csrc/device_common.h",
                   "speculative_decoding_draft_02_amd/csrc/qknorm_insert_kernel.hip",
                   "speculative_decoding_draft_02_amd/csrc/qknorm_insert.cpp",
