@@ -590,6 +590,11 @@ def main():
                 "input_sets": n_sets,
                 "wall_s": r["wall_s"],
             }
+            if setup.wl.fp8:
+                # e4m3 codes at +-448 (0x7E / 0xFE) left in the caches: the
+                # saturating store at work (the V probes of the fp8 prefill)
+                results[name]["saturated_codes_in_caches"] = int(sum(
+                    int(((a.kv_cache == 0x7E) | (a.kv_cache == 0xFE)).sum()) for a in setup.layers))
         results[name]["pct_of_hbm_peak"] = 100.0 * results[name].get("kernel_GB_s", results[name]["GB_s"]) / HBM_PEAK_GBS
         if not args.no_unfused:
             # the base path the fused write replaces, on the same inputs and caches

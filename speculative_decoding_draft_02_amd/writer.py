@@ -43,6 +43,31 @@ def _split_slot_mapping(slot_mapping, num_layers):
     return None, maps
 
 
+def check_write_preconditions(positions: torch.Tensor, slot_mapping, cos_sin_rows: int,
+                              num_blocks: int, block_size: int) -> None:
+    """The write's preconditions that the kernel does not check (as on the
+    vLLM API page "vllm.models.minimax_m3.common.ops.dspark_context_kv"):
+    every non-padding token's position indexes the cos/sin table, every
+    slot is inside the cache, and no two non-padding tokens of a layer share
+    a slot.  Raises ValueError naming the first violation.  Costs a host
+    sync: meant for debugging (DSparkContextKVWriter(debug_checks=True))."""
+    maps = [slot_mapping] if isinstance(slot_mapping, torch.Tensor) and slot_mapping.dim() == 1 \
+        else list(slot_mapping)
+    capacity = int(num_blocks) * int(block_size)
+    for l, slots in enumerate(maps):
+        valid = slots >= 0
+        pos = positions[valid]
+        if pos.numel() and (bool((pos < 0).any()) or bool((pos >= cos_sin_rows).any())):
+            raise ValueError(f"a position is outside the cos/sin table of {cos_sin_rows} rows "
+                             f"(slot mapping {l})")
+        s = slots[valid]
+        if s.numel() and bool((s >= capacity).any()):
+            raise ValueError(f"a slot is >= num_blocks * block_size = {capacity} "
+                             f"(slot mapping {l})")
+        if s.numel() != torch.unique(s).numel():
+            raise ValueError(f"two tokens share a slot (slot mapping {l})")
+
+
 @dataclass
 class AttnLayer:
     """The attributes of a draft attention layer that the writer reads."""
@@ -55,7 +80,11 @@ class AttnLayer:
 class DSparkContextKVWriter:
     """Writes precomputed context K/V into every draft layer's KV cache."""
 
-    def __init__(self, attn_layers) -> None:
+    def __init__(self, attn_layers, debug_checks: bool = False) -> None:
+        """debug_checks: check the preconditions the kernel trusts (positions
+        in the table, slots in the cache, no shared slots) on every call,
+        at the cost of a host sync per call."""
+        self._debug_checks = bool(debug_checks)
         layers = list(attn_layers)
         error = self._validate(layers)
         if error is not None:
@@ -197,6 +226,10 @@ class DSparkContextKVWriter:
             raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}, "
                              f"expected (rows, {rotary_dim})")
         self._ensure_tables()
+        if self._debug_checks:
+            c0 = self._layers[0].kv_cache
+            check_write_preconditions(positions, shared if shared is not None else per_layer,
+                                      cos_sin_cache.shape[0], c0.shape[0], c0.shape[2])
         stream = torch.cuda.current_stream(dev).cuda_stream
         if shared is not None:
             st = _lib.dspark_ctx_kv_writer_write(

@@ -186,3 +186,51 @@ def run_insert_oracle(oracle, wl, **kw):
         wl.positions, wl.cos_sin, wl.rotary_dim, slot_mapping=wl.slot_mapping, cache=cache,
         fp8=wl.fp8, k_scale=wl.k_scale, v_scale=wl.v_scale, want_q_fp8=wl.q_fp8,
         q_scale=wl.q_scale, **kw)
+
+
+# ------------------------------------------------------------------------
+# A third implementation of the write, in numpy float32 arithmetic written
+# out literally: the 128-term sum of squares added sequentially in fp32,
+# rsqrt as 1 / sqrt in fp32, the products and RoPE terms each rounded to
+# fp32, then bf16 (and e4m3 of the fp32 quotient for fp8 caches).
+
+def numpy_f32_write(wl):
+    f32 = np.float32
+    N, L, _, H, D = wl.all_kv.shape
+    R = wl.rotary_dim
+    k = bits_to_f32(wl.all_kv[:, :, 0]).astype(f32)               # [N, L, H, D]
+    v = wl.all_kv[:, :, 1]
+    w = bits_to_f32(wl.k_norm_weight).astype(f32)                 # [L, D]
+    ss = np.zeros((N, L, H), f32)
+    for i in range(D):                                            # sequential fp32 sum
+        ss = (ss + k[..., i] * k[..., i]).astype(f32)
+    r = (f32(1.0) / np.sqrt((ss / f32(D) + f32(wl.eps)).astype(f32))).astype(f32)
+    xr = (k * r[..., None]).astype(f32)
+    y = bits_to_f32(bf16_bits((xr * (f32(1.0) + w[None, :, None, :])).astype(f32))).astype(f32)
+    cs = bits_to_f32(wl.cos_sin[wl.positions]).astype(f32)        # [N, R]
+    c = cs[:, None, None, : R // 2]
+    s = cs[:, None, None, R // 2:]
+    a, b = y[..., : R // 2], y[..., R // 2: R]
+    out = y.copy()
+    out[..., : R // 2] = bits_to_f32(bf16_bits((a * c - b * s).astype(f32)))
+    out[..., R // 2: R] = bits_to_f32(bf16_bits((b * c + a * s).astype(f32)))
+    kb = bf16_bits(out)                                           # [N, L, H, D] codes
+    caches = wl.new_host_caches()
+    slots = wl.slot_mapping
+    for l in range(L):
+        sl = slots[l] if slots.ndim == 2 else slots
+        for t in np.flatnonzero(sl >= 0):
+            blk, off = sl[t] // wl.block_size, sl[t] % wl.block_size
+            for h in range(H):
+                row = caches[l][blk, h, off]
+                if wl.fp8:
+                    kq = torch.from_numpy(np.clip(bits_to_f32(kb[t, l, h]) / f32(wl.k_scales[l]),
+                                                  -448, 448).astype(f32))
+                    vq = torch.from_numpy(np.clip(bits_to_f32(v[t, l, h]) / f32(wl.v_scales[l]),
+                                                  -448, 448).astype(f32))
+                    row[:128] = kq.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                    row[128:] = vq.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                else:
+                    row[:128] = kb[t, l, h]
+                    row[128:] = v[t, l, h]
+    return caches

@@ -324,3 +324,22 @@ def test_hidden_norm_and_project_write_argument_checks(lib):
         assert reason in E(), (kw, E())
     assert pw(num_ctx=0) == _lib.OK                                    # no launch
     _lib.dspark_ctx_kv_writer_destroy(w)
+
+
+def test_debug_precondition_checks_on_cpu_tensors():
+    import torch
+    from speculative_decoding_draft_02_amd.writer import check_write_preconditions as chk
+    pos = torch.tensor([0, 5, 9, 3])
+    ok = torch.tensor([3, -1, 7, 0])
+    chk(pos, ok, 10, 2, 4)                                    # fine: slots < 8, positions < 10
+    chk(torch.tensor([0, 99, 1, 2]), ok, 10, 2, 4)            # padding token's position unused
+    with pytest.raises(ValueError, match="outside the cos/sin table"):
+        chk(torch.tensor([0, 5, 10, 3]), ok, 10, 2, 4)
+    with pytest.raises(ValueError, match="num_blocks"):
+        chk(pos, torch.tensor([3, -1, 8, 0]), 10, 2, 4)
+    with pytest.raises(ValueError, match="share a slot"):
+        chk(pos, torch.tensor([3, 3, 7, 0]), 10, 2, 4)
+    # per-layer mappings: each layer on its own
+    chk(pos, [ok, torch.tensor([1, 2, 3, 4])], 10, 2, 4)
+    with pytest.raises(ValueError, match="slot mapping 1"):
+        chk(pos, [ok, torch.tensor([1, 1, 3, 4])], 10, 2, 4)

@@ -266,3 +266,30 @@ def test_per_layer_slot_list_forms():
     for other in res[1:]:
         for a, b in zip(res[0], other):
             assert np.array_equal(a, b)
+
+
+def test_debug_checks_refuse_bad_inputs_before_launch(oracle_lib):
+    """With debug_checks the writer refuses a shared slot or an out-of-table
+    position before any launch (the caches stay untouched), and writes as
+    usual otherwise."""
+    wl = W.make(0)
+    layers = make_layers(wl)
+    writer = DSparkContextKVWriter(layers, debug_checks=True)
+    x = DeviceInputs(wl)
+    bad = x.slots.clone()
+    valid = torch.nonzero(bad >= 0).flatten()
+    bad[valid[1]] = bad[valid[0]]
+    with pytest.raises(ValueError, match="share a slot"):
+        writer(x.all_kv, x.w, x.eps, x.positions, x.cos_sin, x.rotary_dim, bad)
+    far = x.positions.clone()
+    far[valid[0]] = x.cos_sin.shape[0]
+    with pytest.raises(ValueError, match="cos/sin table"):
+        writer(x.all_kv, x.w, x.eps, far, x.cos_sin, x.rotary_dim, x.slots)
+    torch.cuda.synchronize()
+    assert all(bool((cache_codes(a.kv_cache) == wl.sentinel).all()) for a in layers)
+    x.call(writer)
+    torch.cuda.synchronize()
+    ref = run_oracle(oracle_lib, wl)
+    got = [cache_codes(a.kv_cache) for a in layers]
+    assert C.compare(got, ref, wl.slot_mapping, wl.fp8, wl.sentinel).failures == 0
+    writer.close()

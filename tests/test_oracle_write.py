@@ -352,3 +352,29 @@ def test_oracle_identical_per_layer_slots_equal_shared(oracle_lib):
                             np.stack([wl.slot_mapping] * 4), per, False)
     for a, b in zip(shared, per):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["tiny", "decode", "sweep-fp8", "sweep-bf16", "all-padding"])
+def test_oracle_vs_numpy_float32_literal(oracle_lib, case):
+    """A third implementation in literal numpy float32 arithmetic (sequential
+    fp32 sum, fp32 rsqrt, fp32 products) meets the acceptance rule against
+    the exact oracle, with nearly every K bit-exact."""
+    from _util import numpy_f32_write
+    if case == "tiny":
+        wl = W.make(0)
+    elif case == "decode":
+        wl = compact_blocks(W.make(4))
+    elif case == "sweep-fp8":
+        wl = W.custom(37, 3, 3, 64, 8, 7, True, seed=5, pad_fraction=0.1, kv_std=4.0)
+    elif case == "sweep-bf16":
+        wl = W.custom(50, 2, 4, 16, 4, 16, False, seed=6, pad_fraction=0.2)
+    else:
+        wl = W.custom(4, 1, 1, 32, 2, 4, False, seed=7, pad_fraction=1.0)
+    ref = numpy_f32_write(wl)
+    res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                  wl.rotary_dim, wl.slot_mapping, wl.new_host_caches(), wl.fp8,
+                                  wl.k_scales, wl.v_scales)
+    rep = C.compare(ref, res, wl.slot_mapping, wl.fp8, wl.sentinel)
+    tot = rep.totals()
+    assert rep.failures == 0, tot
+    assert tot["k"]["exact"] >= 0.99 * tot["k"]["n"]
