@@ -38,10 +38,12 @@ int dspark_hidden_norm(const void *x, int64_t rows, int32_t dim, const void *wei
 /* The projection all_kv = bf16(states @ kv_weight^T) with the context write
  * of dspark_ctx_kv_writer_write applied to it in the same kernel:
  *   states     bf16 [num_ctx, hidden], the hidden-norm output, contiguous,
- *              16-byte aligned; hidden a positive multiple of 64
+ *              16-byte aligned; hidden a positive multiple of 64;
+ *              (num_ctx + 256) * hidden * 2 below 2^31 bytes
  *   kv_weight  bf16 [num_layers * 2 * num_kv_heads * 128, hidden], a linear
  *              layer's [out, in] weight whose output row is ordered as
- *              all_kv's (layer, K/V, kv head, dim), 16-byte aligned
+ *              all_kv's (layer, K/V, kv head, dim), 16-byte aligned, below
+ *              2^31 bytes
  * and the remaining arguments exactly as for dspark_ctx_kv_writer_write
  * (the writer's layers, kv heads, caches and scales; k_norm_weight, eps,
  * positions, cos_sin_cache, rotary_dim, slot_mapping, and its

@@ -70,6 +70,12 @@ extern "C" int dspark_ctx_kv_writer_project_write(
         return fail(DSPARK_E_ARG, "positions and slot_mapping must be 8-byte aligned");
     if (cos_sin_rows <= 0)
         return fail(DSPARK_E_ARG, "cos_sin_cache has no rows");
+    // the kernel addresses states and kv_weight with 32-bit byte offsets
+    // (one tile of 256 rows past the end included)
+    const int64_t cols = int64_t{num_layers} * 2 * num_kv_heads * DSPARK_HEAD_DIM;
+    if ((num_ctx + 256) * hidden * 2 >= (int64_t{1} << 31) || cols * hidden * 2 >= (int64_t{1} << 31))
+        return fail(DSPARK_E_ARG, "states or kv_weight exceed 2 GiB (num_ctx %lld, hidden %d)",
+                    (long long)num_ctx, hidden);
     if (num_ctx == 0)
         return DSPARK_OK;
 

@@ -319,6 +319,7 @@ def test_hidden_norm_and_project_write_argument_checks(lib):
         (dict(states=fake + 8), "16-byte aligned"),
         (dict(positions=fake + 4), "8-byte aligned"),
         (dict(cos_sin_rows=0), "no rows"),
+        (dict(num_ctx=200000, hidden=6144), "exceed 2 GiB"),
     ]:
         assert pw(**kw) == _lib.E_ARG, kw
         assert reason in E(), (kw, E())
