@@ -378,3 +378,39 @@ def test_oracle_vs_numpy_float32_literal(oracle_lib, case):
     tot = rep.totals()
     assert rep.failures == 0, tot
     assert tot["k"]["exact"] >= 0.99 * tot["k"]["n"]
+
+
+# Brute-force tiny sweep: every combination of L in {1, 2}, nkv in {1, 2},
+# R in {16, 32, 64}, block size in {1, 2, 16} and both cache dtypes, with
+# N <= 4 tokens and three slot patterns (no padding, half padding, every slot
+# padding).  Both independent fp32 implementations must meet the acceptance
+# rule against the exact oracle on every case.
+TINY_SWEEP = [(L, nkv, R, bs, fp8)
+              for L in (1, 2) for nkv in (1, 2) for R in (16, 32, 64)
+              for bs in (1, 2, 16) for fp8 in (False, True)]
+
+
+@pytest.mark.parametrize("R", [16, 32, 64])
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_brute_force_tiny_sweep(oracle_lib, R, fp8):
+    from _util import numpy_f32_write
+    cases = 0
+    for i, (L, nkv, r, bs, f) in enumerate(TINY_SWEEP):
+        if r != R or f != fp8:
+            continue
+        for pad in (0.0, 0.5, 1.0):
+            N = 1 + (i + int(4 * pad)) % 4
+            nb = max(1, -(-N // bs)) + 1
+            wl = W.custom(N, L, nkv, R, bs, nb, fp8, seed=7919 * i + int(10 * pad),
+                          pad_fraction=pad, kv_std=4.0 if fp8 else 1.0)
+            res = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions,
+                                          wl.cos_sin, R, wl.slot_mapping, wl.new_host_caches(),
+                                          fp8, wl.k_scales, wl.v_scales)
+            for name, ref in (("torch", torch_unfused(wl)), ("numpy", numpy_f32_write(wl))):
+                rep = C.compare(ref, res, wl.slot_mapping, fp8, wl.sentinel)
+                assert rep.failures == 0, (name, L, nkv, R, bs, fp8, pad, rep.summary())
+            if pad == 1.0:
+                # every slot is padding: nothing at all is written
+                assert all(np.all(c == wl.sentinel) for c in res.caches)
+            cases += 1
+    assert cases == 12 * 3
