@@ -69,9 +69,14 @@ def bf16_dev(bits, dev):
 class Setup:
     """Caches + writer for a workload shape, and `n_sets` input sets."""
 
-    def __init__(self, index: int, n_sets: int, dev, layer_slots: bool = False):
+    def __init__(self, index: int, n_sets: int, dev, layer_slots: bool = False, tp: int = 1):
         self.index = index
         self.sets = [W.make(index, variant=v) for v in range(n_sets)]
+        if tp > 1:
+            # every rank's share of every set, each in relocated blocks: a
+            # cycle still reads and writes more than the last-level cache
+            self.sets = [W.relocate_blocks(W.head_shard(s, tp, r), seed=31 * v + r)
+                         for v, s in enumerate(self.sets) for r in range(tp)]
         if layer_slots:
             self.sets = [W.per_layer_slots(s, seed=77 + v, pad_fraction=0.02)
                          for v, s in enumerate(self.sets)]
@@ -625,6 +630,26 @@ def main():
         results["prefill_bf16_layer_slots"]["pct_of_hbm_peak"] = \
             100.0 * results["prefill_bf16_layer_slots"]["kernel_GB_s"] / HBM_PEAK_GBS
         log("prefill_bf16_layer_slots", json.dumps(results["prefill_bf16_layer_slots"]))
+        del setup
+        torch.cuda.empty_cache()
+
+    if args.workload in ("all", "prefill_bf16"):
+        # one rank's share of the prefill write under 4-way head parallelism
+        # (2 of the 8 kv heads): the shape a single GPU of a TP-4 group writes
+        log("workload prefill_bf16_tp4_shard setup")
+        setup = Setup(HEADLINE, args.sets, dev, tp=4)
+        r = time_eager(setup, args.steps, args.warmup, stream)
+        avg = r["region_s"] / args.steps
+        res = {
+            "ms_per_step": avg * 1e3, "GB_s": float(r["bytes"].sum() / r["region_s"] / 1e9),
+            "kernel_us_avg": avg * 1e6, "kernel_GB_s": float(r["bytes"].mean() / avg / 1e9),
+            "token_layers_per_s": float(r["token_layers"].sum() / r["region_s"]),
+            "bytes_per_call": int(r["bytes"].mean()), "input_sets": len(setup.sets),
+            "note": "one rank's 2 of 8 kv heads (nkv = 2), the prefill's tokens and positions; "
+                    "input sets = every rank's heads of each prefill set, blocks relocated"}
+        res["pct_of_hbm_peak"] = 100.0 * res["kernel_GB_s"] / HBM_PEAK_GBS
+        results["prefill_bf16_tp4_shard"] = res
+        log("prefill_bf16_tp4_shard", json.dumps(res))
         del setup
         torch.cuda.empty_cache()
 

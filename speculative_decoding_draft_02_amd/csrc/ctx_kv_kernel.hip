@@ -50,6 +50,19 @@ namespace {
 // the fp8 prefill, whose longer arithmetic favours finer scheduling, and
 // slower on small writes, which then spread over fewer CUs).
 constexpr int kWideBlockMinWaves = 4096;
+// Writes of at most this many 4-row waves give each layer its own wave
+// (bf16 caches, fp8 caches: the fp8 store's longer arithmetic gains up to
+// larger writes).  Measured under graph replay, L = 5: the split saves 0.7 us
+// of 3.2 on a 300-wave decode write and 6% at 1500 waves (bf16) and 2400
+// (fp8), and loses 8-14% at 2000 (bf16) and 4000 (fp8) waves.
+#ifndef DSPARK_SPLIT_MAX_WAVES_BF16
+#define DSPARK_SPLIT_MAX_WAVES_BF16 1536
+#endif
+#ifndef DSPARK_SPLIT_MAX_WAVES_FP8
+#define DSPARK_SPLIT_MAX_WAVES_FP8 3072
+#endif
+constexpr uint32_t kSplitMaxWavesBf16 = DSPARK_SPLIT_MAX_WAVES_BF16;
+constexpr uint32_t kSplitMaxWavesFp8 = DSPARK_SPLIT_MAX_WAVES_FP8;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
@@ -64,13 +77,19 @@ constexpr int kNumXcds = 8;
 // token's slot and position are wave-uniform (scalar loads, scalar exit).
 // kLayerSlots: every layer has its own slot mapping (layers in different KV
 // cache groups); always with the general row mapping.
+// kLayerSplit (small writes, kChunk = 1): each wave writes one layer of its 4
+// rows; wave w takes layer w % L of row group w / L.  A small batch then
+// spreads over L times more waves, each with an L-th of the arithmetic.
 template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform, bool kLayerSlots,
-          int kWavesPerBlock>
+          bool kLayerSplit, int kWavesPerBlock>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const CtxKvArgs a) {
+    static_assert(!kLayerSplit || (kChunk == 1 && kSinglePass && !kLayerSlots),
+                  "a split wave holds one layer");
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4;        // quarter: which of the wave's 4 rows
     const int c = lane & 15;        // 16-byte chunk: elements 8c .. 8c+7
-    const int L = kSinglePass ? kChunk : a.num_layers;
+    const int L = kSinglePass ? kChunk : a.num_layers;       // layers this wave writes
+    const int Lrow = kLayerSplit ? a.num_layers : L;         // layers per all_kv token row
     const int nkv = a.nkv;
 
     uint32_t block = blockIdx.x;
@@ -79,8 +98,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         const uint32_t full = gridDim.x - gridDim.x % kNumXcds;
         if (block < full) block = (block % kNumXcds) * (full / kNumXcds) + block / kNumXcds;
     }
-    const uint32_t wave = block * kWavesPerBlock +
-                          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    uint32_t wave = block * kWavesPerBlock +
+                    static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    int l0 = 0;                     // first layer this wave writes
+    if constexpr (kLayerSplit) {
+        const uint32_t nl = static_cast<uint32_t>(a.num_layers);
+        l0 = static_cast<int>(wave % nl);
+        wave /= nl;
+    }
     const uint32_t unit0 = wave * kRowsPerWave;             // first row of the wave
     if (unit0 >= a.num_units) return;
 
@@ -91,7 +116,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     int64_t lslot[kChunk];          // per-layer slots (kLayerSlots only)
     bool in_range = true;
     const int64_t kv_stride = static_cast<int64_t>(nkv) * 16;    // K_l -> V_l (uint4 units)
-    const uint4 *w_base = reinterpret_cast<const uint4 *>(a.k_norm_weight) + c;
+    const uint4 *w_base = reinterpret_cast<const uint4 *>(a.k_norm_weight) + l0 * 16 + c;
     const uint4 *kv_base;
     // every K, V and weight load of the chunk goes out before any arithmetic;
     // all_kv[t, l, kv, h, 8c..8c+7] = kv_base + (l * 2 + kv) * nkv * 16
@@ -109,7 +134,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         t = unit0 / static_cast<uint32_t>(nkv);
         h = static_cast<int>(unit0 - t * static_cast<uint32_t>(nkv)) + q;
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
-                  (static_cast<int64_t>(t) * L * 2 * nkv + h) * 16 + c;
+                  ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         slot = a.slots[t];
         pos = a.positions[t];
         // The row loads do not depend on the slot: they go out together with
@@ -132,7 +157,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         slot = 0;
         pos = a.positions[t];
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
-                  (static_cast<int64_t>(t) * L * 2 * nkv + h) * 16 + c;
+                  ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         load_chunk(0);
         asm volatile("" ::: "memory");   // keep the loads ahead of the predicated stores
     } else {
@@ -158,7 +183,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             slot = read_lane64(slot, src);
         }
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
-                  (static_cast<int64_t>(t) * L * 2 * nkv + h) * 16 + c;
+                  ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         load_chunk(0);
     }
 
@@ -181,8 +206,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) {
                 if (lb + j < L) {
-                    if (lane == 2 * j) { soff = a.kscale_off[lb + j]; has = true; }
-                    if (lane == 2 * j + 1) { soff = a.vscale_off[lb + j]; has = true; }
+                    if (lane == 2 * j) { soff = a.kscale_off[l0 + lb + j]; has = true; }
+                    if (lane == 2 * j + 1) { soff = a.vscale_off[l0 + lb + j]; has = true; }
                 }
             }
             if (has) my_scale = a.scale0[soff];
@@ -194,7 +219,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             if (l >= L) break;
             uint32_t kb[4];
             norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb);
-            int64_t base = a.cache_off[l] + row;
+            int64_t base = a.cache_off[l0 + l] + row;
             bool store = true;
             if constexpr (kLayerSlots) {
                 const int64_t s = lslot[j];
@@ -238,19 +263,38 @@ void launch_wpb(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const dim3 block(64 * kWavesPerBlock);
     if (a.layer_slots_on)
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, true,
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, true, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
     else if (a.nkv % kRowsPerWave == 0)
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, false,
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, false, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, false,
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, false, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
+}
+
+// One wave per (row group, layer), four waves per workgroup.
+template <int R, bool kFp8>
+void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
+    const uint32_t split = waves * static_cast<uint32_t>(a.num_layers);
+    const dim3 grid((split + 3) / 4);
+    const dim3 block(256);
+    if (a.nkv % kRowsPerWave == 0)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, true, false, true, 4>),
+                           grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, false, false, true, 4>),
+                           grid, block, 0, stream, a);
 }
 
 template <int R, bool kFp8, int kChunk, bool kSinglePass>
 void launch_one(const CtxKvArgs &a, hipStream_t stream) {
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
+    if (!a.layer_slots_on && a.num_layers > 1 &&
+        waves <= (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)) {
+        launch_split<R, kFp8>(a, waves, stream);
+        return;
+    }
     if constexpr (!kFp8) {
         if (waves >= kWideBlockMinWaves) {
             launch_wpb<R, kFp8, kChunk, kSinglePass, 8>(a, waves, stream);

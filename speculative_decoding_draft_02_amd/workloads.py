@@ -251,6 +251,35 @@ def per_layer_slots(wl: Workload, seed: int, pad_fraction: float = 0.05) -> Work
     return dataclasses.replace(wl, slot_mapping=maps)
 
 
+def head_shard(wl: Workload, tp: int, rank: int) -> Workload:
+    """One rank's share under head (tensor) parallelism: kv heads
+    [rank * nkv / tp, (rank + 1) * nkv / tp) of every token and layer, written
+    into caches that hold only those heads.  Slots, positions, norm weights
+    and the cos/sin table are the same on every rank."""
+    import dataclasses
+    nkv = wl.num_kv_heads
+    if tp < 1 or nkv % tp or not 0 <= rank < tp:
+        raise ValueError("tp must divide num_kv_heads and 0 <= rank < tp")
+    h = nkv // tp
+    part = np.ascontiguousarray(wl.all_kv[:, :, :, rank * h:(rank + 1) * h, :])
+    return dataclasses.replace(wl, name="%s_tp%d_rank%d" % (wl.name, tp, rank),
+                               num_kv_heads=h, all_kv=part)
+
+
+def relocate_blocks(wl: Workload, seed: int) -> Workload:
+    """The same tokens placed in other cache blocks: every block of a shared
+    slot mapping is moved by one random permutation of the blocks (offsets in
+    a block and padding kept), so requests stay block-contiguous."""
+    import dataclasses
+    if wl.slot_mapping.ndim != 1:
+        raise ValueError("relocate_blocks takes a shared slot mapping")
+    perm = np.random.default_rng(seed).permutation(wl.num_blocks)
+    s = wl.slot_mapping
+    bs = wl.block_size
+    moved = np.where(s >= 0, perm[np.maximum(s, 0) // bs] * bs + np.maximum(s, 0) % bs, s)
+    return dataclasses.replace(wl, slot_mapping=moved.astype(np.int64))
+
+
 def custom(num_ctx, num_layers, num_kv_heads, rotary_dim, block_size, num_blocks,
            fp8, seed, pad_fraction=0.1, kv_std=1.0, w_std=0.1, cs_rows=None,
            eps=1e-6) -> Workload:

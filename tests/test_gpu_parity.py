@@ -44,6 +44,15 @@ def test_workload_parity(oracle_lib, index):
     assert tot["v"]["exact"] == tot["v"]["n"]
 
 
+@pytest.mark.parametrize("rank", [0, 3])
+def test_head_shard_parity(oracle_lib, rank):
+    """One rank's share of the 4096-token bf16 prefill under 4-way head
+    parallelism (2 of 8 kv heads, the general row mapping), at full size."""
+    wl = W.head_shard(W.make(1), 4, rank)
+    tot = _check(oracle_lib, wl)
+    assert tot["v"]["exact"] == tot["v"]["n"]
+
+
 SWEEP = [
     # N, L, nkv, R, bs, blocks, fp8, pad
     (1, 1, 1, 16, 1, 1, False, 0.0),
@@ -59,6 +68,11 @@ SWEEP = [
     (33, 4, 5, 64, 32, 4, False, 0.0),
     (257, 6, 7, 16, 2, 200, True, 0.25),
     (16, 2, 2, 32, 16, 1, False, 1.0),      # every token is padding
+    # large enough that each wave writes every layer (no per-layer split)
+    (2100, 3, 3, 16, 16, 200, False, 0.2),
+    (3200, 9, 2, 64, 8, 512, False, 0.1),   # L > 8 in chunks
+    (4200, 12, 3, 32, 4, 1200, True, 0.1),  # L > 8 in chunks, fp8
+    (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8
 ]
 
 

@@ -414,3 +414,40 @@ def test_brute_force_tiny_sweep(oracle_lib, R, fp8):
                 assert all(np.all(c == wl.sentinel) for c in res.caches)
             cases += 1
     assert cases == 12 * 3
+
+
+@pytest.mark.parametrize("tp", [2, 4])
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_head_shards_reassemble_the_full_write(oracle_lib, tp, fp8):
+    """Head parallelism needs no exchange: each rank writing only its kv
+    heads into caches holding only those heads gives exactly those heads of
+    the full write, and nothing else."""
+    wl = W.custom(40, 3, 4, 32, 8, 8, fp8, seed=11, pad_fraction=0.2,
+                  kv_std=4.0 if fp8 else 1.0)
+    full = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                   wl.rotary_dim, wl.slot_mapping, wl.new_host_caches(), fp8,
+                                   wl.k_scales, wl.v_scales)
+    h = wl.num_kv_heads // tp
+    for r in range(tp):
+        sh = W.head_shard(wl, tp, r)
+        assert sh.num_kv_heads == h and sh.cache_shape[1] == h
+        part = oracle_lib.ctx_kv_write(sh.all_kv, sh.k_norm_weight, sh.eps, sh.positions,
+                                       sh.cos_sin, sh.rotary_dim, sh.slot_mapping,
+                                       sh.new_host_caches(), fp8, sh.k_scales, sh.v_scales)
+        for a, b in zip(part.caches, full.caches):
+            assert np.array_equal(a, b[:, r * h:(r + 1) * h])
+    with pytest.raises(ValueError):
+        W.head_shard(wl, 3, 0)
+
+
+def test_relocated_blocks_keep_block_structure():
+    wl = W.make(0)
+    moved = W.relocate_blocks(wl, seed=4)
+    s, m = wl.slot_mapping, moved.slot_mapping
+    assert np.array_equal(s < 0, m < 0)
+    assert np.array_equal(s[s >= 0] % wl.block_size, m[m >= 0] % wl.block_size)
+    # same block before means same block after; slots stay unique and in range
+    b, mb = s[s >= 0] // wl.block_size, m[m >= 0] // wl.block_size
+    assert np.array_equal(b[:, None] == b[None, :], mb[:, None] == mb[None, :])
+    assert np.unique(m[m >= 0]).size == m[m >= 0].size
+    assert m.max() < wl.num_blocks * wl.block_size
