@@ -14,20 +14,21 @@
 // The projection is a dense contraction, so it runs on the matrix cores:
 // v_mfma_f32_32x32x16_bf16 (lane l holds A[l % 32][8 (l / 32) + i] and
 // B[8 (l / 32) + i][l % 32], i < 8; accumulator register i holds
-// D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).  A workgroup of 8 waves (two per
-// SIMD) owns a 256-token x 256-column tile; each wave computes 64 tokens x 128
-// columns, and 128 columns are exactly one (layer, kv, head) row of all_kv, so
-// the write's per-row norm, RoPE and store happen on data the wave holds.  The
-// weight is the MFMA's first operand, so a lane ends with one token's values
-// in runs of 4 consecutive columns (half of the head; lane l ^ 32 holds the
-// other half): the norm's sum of squares is local adds and one exchange, and
-// every RoPE partner column is in the same lane.  Operands are read through
-// buffer resources (rows past num_ctx read as zero) into registers two k
-// slices ahead, then into double-buffered LDS whose 16-byte chunks are
-// XOR-swizzled so that the stores and the MFMA operand reads are free of
-// bank conflicts.  The epilogue stages the tile's cos/sin rows in LDS, writes
-// the finished rows to LDS and stores whole 256-byte (bf16) or 128-byte
-// (e4m3) cache half rows per 16 lanes.
+// D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).  A workgroup of 4 waves (one per
+// SIMD) owns a 256-token x 256-column tile; each wave computes 128 tokens x
+// 128 columns, and 128 columns are exactly one (layer, kv, head) row of
+// all_kv, so the write's per-row norm, RoPE and store happen on data the wave
+// holds.  The weight is the MFMA's first operand, so a lane ends with one
+// token's values in runs of 4 consecutive columns (half of the head; lane
+// l ^ 32 holds the other half): the norm's sum of squares is local adds and
+// one exchange, and every RoPE partner column is in the same lane.  Operands
+// go from memory straight into a ring of LDS stages (buffer loads with the
+// lds bit; rows past num_ctx read as zero), whose 16-byte chunks are
+// XOR-swizzled so that the MFMA operand reads are free of bank conflicts.
+// The epilogue stages the tile's cos/sin rows in LDS, writes the finished
+// rows to LDS and stores whole 256-byte (bf16) or 128-byte (e4m3) cache half
+// rows per 16 lanes.
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,201 +83,30 @@ __global__ __launch_bounds__(256) void hidden_norm_kernel(const uint16_t *x, con
 
 // --------------------------------------------- projection + write epilogue --
 
-// Tile geometry: WM x WN waves; a wave computes 4 x TI MFMA tiles of 32 x 32,
-// i.e. 128 columns = exactly one (layer, kv, head) row of all_kv for 32 TI
-// tokens.  A workgroup tile is (32 TI WM) tokens x (128 WN) columns, k slices
-// of 64; DEPTH k slices are in flight in registers.
-constexpr int kPK = 64;
 constexpr int kPNumXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// position of 16-byte chunk j (of 8) of LDS row r: XOR with (r / 2) % 8 makes
-// 16 consecutive rows at one logical chunk hit 16 distinct bank groups
-__device__ __forceinline__ int swz(int r, int j) { return (r << 3) + (j ^ ((r >> 1) & 7)); }
-
 __device__ __forceinline__ float round_bf16(float v) { return bf16_lo(pack_bf16(v, 0.0f)); }
 
 
-template <int WM, int WN, int TI>
-struct Tile {
-    static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int kBM = 32 * TI * WM;        // tokens
-    static constexpr int kBN = 128 * WN;            // columns
-    static constexpr int kA = kBM * kPK / 8;        // 16-byte chunks of an A slice
-    static constexpr int kB = kBN * kPK / 8;
-    static constexpr int kStage = kA + kB;
-    static constexpr int kPA = kA / kThreads;       // A chunks per thread per slice
-    static constexpr int kPB = kB / kThreads;
-    static constexpr int kRowStep = kThreads / 8;   // rows covered by one pass of the threads
-    // LDS: two stages, then the staged cos/sin rows (up to R = 64)
-    static constexpr int kCsOff = 2 * kStage;       // in 16-byte chunks
-    static constexpr int kLds = kCsOff + kBM * 64 * 2 / 16;
-    static_assert(kBM * kBN * 2 <= 2 * kStage * 16, "the finished tile must fit the stages");
-};
-
-template <int R, bool kFp8, int WM, int WN, int TI, int DEPTH>
-__global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const ProjArgs a) {
-    using T = Tile<WM, WN, TI>;
-    __shared__ u32x4 lds[T::kLds];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv % WM;
-    const int wn = wv / WM;
-    const uint32_t mblocks = (a.num_ctx + T::kBM - 1) / T::kBM;
-
-    // XCD-aware tile order: XCD x (workgroup i runs on XCD i % 8) takes a
-    // contiguous run of tiles; tiles are M-fastest, so an XCD works through a
-    // few heads' weight slices while all token tiles pass through its L2
-    uint32_t bid = blockIdx.x;
-    const uint32_t full = gridDim.x - gridDim.x % kPNumXcds;
-    if (bid < full) bid = (bid % kPNumXcds) * (full / kPNumXcds) + bid / kPNumXcds;
-    const uint32_t mb = bid % mblocks;
-    const uint32_t nb = bid / mblocks;
-    const int64_t m0 = static_cast<int64_t>(mb) * T::kBM;
-    const int64_t n0 = static_cast<int64_t>(nb) * T::kBN;
-
-    // global -> LDS copy roles: chunk j of rows r0 + kRowStep p.  Operands
-    // are read through buffer resources: one per-lane byte offset, the row
-    // step and the k slice in scalar offsets, and token rows past num_ctx
-    // fall outside the resource's range and read as zero (computed, never
-    // stored).  kRowStep is a multiple of 16, so every row a thread copies
-    // has the same chunk swizzle and its LDS slots are constant offsets.
-    static_assert(T::kRowStep % 16 == 0, "one swizzle per copying thread");
-    const int j = tid & 7;
-    const int r0 = tid >> 3;
-    const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.z), 0, static_cast<int>(a.num_ctx * 2u * a.hidden), 0x00020000);
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.W), 0, static_cast<int>(a.cols * 2u * a.hidden), 0x00020000);
-    const int row_bytes = 2 * a.hidden;
-    const int zoff = (static_cast<int>(m0) + r0) * row_bytes + j * 16;
-    const int woff = (static_cast<int>(n0) + r0) * row_bytes + j * 16;
-    const int step_bytes = T::kRowStep * row_bytes;
-    const int aw0 = swz(r0, j);
-    const int bw0 = T::kA + swz(r0, j);
-    // MFMA operand reads: rows wrow + 32 i + cl of A and 128 wn + 32 n + cl
-    // of B, chunk 2 s + hi of the 16-wide k step s; all these rows share the
-    // swizzle (cl / 2) % 8
-    const int hi = lane >> 5;
-    const int cl = lane & 31;
-    const int wrow = 32 * TI * wm;                    // this wave's first token row
-    const int sw = (cl >> 1) & 7;
-    const int arow = (wrow + cl) * 8;
-    const int brow = T::kA + (128 * wn + cl) * 8;
-    int xs[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) xs[s4] = (2 * s4 + hi) ^ sw;
-
-    // the epilogue's per-token inputs, requested now so that their latency
-    // hides behind the main loop: the position of token row tid (for the
-    // cos/sin staging) and the slot of this wave's store row wrow + lane
-    static_assert(32 * TI == 64, "one store row of the wave band per lane");
-    int64_t my_pos = 0;
-    if (tid < T::kBM) {
-        int64_t t = m0 + tid;
-        if (t >= a.num_ctx) t = a.num_ctx - 1;
-        my_pos = a.positions[t];
-    }
-    const int64_t my_slot = (m0 + wrow + lane < a.num_ctx) ? a.slots[m0 + wrow + lane] : -1;
-
-    f32x16 acc[TI][4];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = f32x16{};
-
-    // Two register sets keep two k slices in flight: while the matrix cores
-    // work on slice kt (LDS stage kt % 2), slice kt + 1 is arriving in one
-    // set and slice kt + 2 is requested into the other; slice kt + 1 goes to
-    // LDS after the MFMAs (its stage was last read before the previous
-    // barrier).  The loop is unrolled by two so that both sets are named
-    // statically and stay in registers.  A wave raises its issue priority
-    // while it runs its MFMAs, so that the other wave of its SIMD issues its
-    // loads and LDS traffic in the gaps rather than competing for the
-    // matrix core.
-    constexpr int kP = T::kPA + T::kPB;
-    u32x4 ra[kP], rb[kP];
-    const int nk = a.hidden / kPK;
-#define DSPARK_FETCH(r, kt)                                                              \
-    do {                                                                                 \
-        const int o_ = (kt) * (kPK * 2);                                                 \
-        _Pragma("unroll") for (int p = 0; p < T::kPA; ++p)                               \
-            r[p] = __builtin_amdgcn_raw_buffer_load_b128(zres, zoff, p * step_bytes + o_, 0); \
-        _Pragma("unroll") for (int p = 0; p < T::kPB; ++p)                               \
-            r[T::kPA + p] =                                                              \
-                __builtin_amdgcn_raw_buffer_load_b128(wres, woff, p * step_bytes + o_, 0); \
-    } while (0)
-#define DSPARK_PUT(r, stage)                                                             \
-    do {                                                                                 \
-        _Pragma("unroll") for (int p = 0; p < T::kPA; ++p)                               \
-            lds[(stage) + aw0 + p * T::kRowStep * 8] = r[p];                             \
-        _Pragma("unroll") for (int p = 0; p < T::kPB; ++p)                               \
-            lds[(stage) + bw0 + p * T::kRowStep * 8] = r[T::kPA + p];                    \
-    } while (0)
-    // one k slice: `next` holds slice kt + 1 (arriving), `spare` receives kt + 2
-#define DSPARK_STEP(kt, next, spare)                                                     \
-    do {                                                                                 \
-        const int cur_ = ((kt) & 1) * T::kStage;                                         \
-        if ((kt) + 2 < nk) DSPARK_FETCH(spare, (kt) + 2);                                \
-        __builtin_amdgcn_s_setprio(1);                                                   \
-        _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                  \
-            bf16x8 af[TI], bfr[4];                                                       \
-            _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
-                af[i] = __builtin_bit_cast(bf16x8, lds[cur_ + arow + 256 * i + xs[s]]);  \
-            _Pragma("unroll") for (int n = 0; n < 4; ++n)                                \
-                bfr[n] = __builtin_bit_cast(bf16x8, lds[cur_ + brow + 256 * n + xs[s]]); \
-            _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
-                _Pragma("unroll") for (int n = 0; n < 4; ++n)                            \
-                    acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                 \
-                        bfr[n], af[i], acc[i][n], 0, 0, 0);                              \
-        }                                                                                \
-        __builtin_amdgcn_s_setprio(0);                                                   \
-        if ((kt) + 1 < nk) DSPARK_PUT(next, T::kStage - cur_);                           \
-        __syncthreads();                                                                 \
-    } while (0)
-    DSPARK_FETCH(ra, 0);
-    DSPARK_PUT(ra, 0);
-    if constexpr (DEPTH == 2) {
-        if (nk > 1) DSPARK_FETCH(ra, 1);
-        __syncthreads();
-        for (int kt = 0; kt < nk; kt += 2) {
-            DSPARK_STEP(kt, ra, rb);
-            if (kt + 1 < nk) DSPARK_STEP(kt + 1, rb, ra);
-        }
-    } else {
-        // one slice in flight: slice kt + 1 is requested into the one set
-        // at the top of step kt and stored after its MFMAs
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur_ = (kt & 1) * T::kStage;
-            if (kt + 1 < nk) DSPARK_FETCH(ra, kt + 1);
-            __builtin_amdgcn_s_setprio(1);
-            _Pragma("unroll") for (int s = 0; s < 4; ++s) {
-                bf16x8 af[TI], bfr[4];
-                _Pragma("unroll") for (int i = 0; i < TI; ++i)
-                    af[i] = __builtin_bit_cast(bf16x8, lds[cur_ + arow + 256 * i + xs[s]]);
-                _Pragma("unroll") for (int n = 0; n < 4; ++n)
-                    bfr[n] = __builtin_bit_cast(bf16x8, lds[cur_ + brow + 256 * n + xs[s]]);
-                _Pragma("unroll") for (int i = 0; i < TI; ++i)
-                    _Pragma("unroll") for (int n = 0; n < 4; ++n)
-                        acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[n], af[i], acc[i][n],
-                                                                            0, 0, 0);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            if (kt + 1 < nk) DSPARK_PUT(ra, T::kStage - cur_);
-            __syncthreads();
-        }
-    }
-#undef DSPARK_STEP
-#undef DSPARK_PUT
-#undef DSPARK_FETCH
-
-    // ---------------------------------------------------------- epilogue --
+// The epilogue: this wave's 128 columns are one (layer, kv, head) row of
+// all_kv for its TI * 32 tokens; it normalises and rotates K, converts, and
+// stores whole cache half rows.  cs_lds holds kBM * R bf16 for the tile's
+// cos/sin rows; tile_row(r) is the LDS address of row r (of WN * kBM) of the
+// finished tile, 128 elements of the cache type each.  Every operand read of
+// the main loop must be complete before the call.
+template <int R, bool kFp8, int WM, int WN, int TI, int kBM, class TileRow>
+__device__ __forceinline__ void project_epilogue(const ProjArgs &a, f32x16 (&acc)[TI][4],
+                                                 uint32_t nb, int wn, int wrow, int tid,
+                                                 int lane, int64_t my_pos,
+                                                 const int64_t (&my_slot)[TI / 2],
+                                                 uint16_t *cs_lds, TileRow tile_row) {
     // this wave's 128 columns are all_kv's (layer, kv, head) = a row of the write
     const int head = static_cast<int>(nb) * WN + wn;
+    const int hi = lane >> 5;
+    const int cl = lane & 31;
     const int layer = head / (2 * a.nkv);
     const int kv = (head / a.nkv) & 1;
     const int h = head % a.nkv;
@@ -284,9 +114,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     // c ^ (r % (R / 8)) so that lanes reading one chunk of consecutive rows
     // spread over the banks
     constexpr int kCsMask = R / 8 - 1;
-    uint16_t *cs_lds = reinterpret_cast<uint16_t *>(lds + T::kCsOff);
-    static_assert(T::kThreads >= T::kBM, "one staging thread per token row");
-    if (tid < T::kBM) {
+    static_assert(64 * WM * WN >= kBM, "one staging thread per token row");
+    if (tid < kBM) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.cos_sin + my_pos * R);
         u32x4 *dst = reinterpret_cast<u32x4 *>(cs_lds + tid * R);
 #pragma unroll
@@ -378,7 +207,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                 const float *v = &y[n][4 * q];
                 if constexpr (!kFp8) {
                     uint2 *dst = reinterpret_cast<uint2 *>(
-                        reinterpret_cast<uint16_t *>(lds) + (wn * T::kBM + rho) * 128 + col);
+                        reinterpret_cast<uint16_t *>(tile_row(wn * kBM + rho)) + col);
                     *dst = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
                 } else {
                     int code = 0;
@@ -386,8 +215,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                                                           div_by_scale(v[1], fs, fy, flim), code, false);
                     code = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_scale(v[2], fs, fy, flim),
                                                           div_by_scale(v[3], fs, fy, flim), code, true);
-                    *reinterpret_cast<int *>(reinterpret_cast<uint8_t *>(lds) +
-                                             (wn * T::kBM + rho) * 128 + col) = code;
+                    *reinterpret_cast<int *>(tile_row(wn * kBM + rho) + col) = code;
                 }
             }
     }
@@ -398,10 +226,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
     const int q4 = lane >> 4;
     const int c16 = lane & 15;
     const int64_t bmask = (int64_t{1} << a.bs_log2) - 1;
+#pragma unroll
+    for (int u = 0; u < TI / 2; ++u)
 #pragma unroll 4
-    for (int it = 0; it < 8 * TI; ++it) {
+    for (int it = 16 * u; it < 16 * u + 16; ++it) {
         const int rho = wrow + 4 * it + q4;
-        const int64_t slot = __shfl(my_slot, 4 * it + q4);   // < 0: padding or past num_ctx
+        // < 0: padding or past num_ctx
+        const int64_t slot = __shfl(my_slot[u], 4 * (it - 16 * u) + q4);
         if (slot < 0) continue;
         const int64_t base = a.cache_off[layer] +
                              ((((slot >> a.bs_log2) * a.nkv + h) << a.bs_log2) + (slot & bmask)) *
@@ -409,25 +240,236 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void project_write_kernel(const Pr
                              kv * DSPARK_HEAD_DIM + c16 * 8;
         const int unit = c16 ^ (rho & 15);                   // the row's permuted 8-column unit
         if constexpr (!kFp8) {
-            const u32x4 v = lds[(wn * T::kBM + rho) * 16 + unit];
+            const u32x4 v = reinterpret_cast<const u32x4 *>(tile_row(wn * kBM + rho))[unit];
             store_row16(static_cast<uint16_t *>(a.cache0) + base, make_uint4(v.x, v.y, v.z, v.w));
         } else {
             store_row8(static_cast<uint8_t *>(a.cache0) + base,
-                       reinterpret_cast<const uint2 *>(lds)[(wn * T::kBM + rho) * 16 + unit]);
+                       reinterpret_cast<const uint2 *>(tile_row(wn * kBM + rho))[unit]);
         }
     }
 }
 
-// the tile geometry in use: 8 waves (two per SIMD), 256-token x 256-column
-// tiles, two k slices in flight
-constexpr int kWM = 4, kWN = 2, kTI = 2, kDepth = 2;
+// ------------------------------------------------ the projection kernel --
+//
+// Four waves, each 128 tokens x 128 columns (4 x 4 MFMA tiles, accumulators in
+// the AGPRs): per 16-wide k step a wave reads 8 KB of operands from LDS for
+// 16 MFMAs (two waves per SIMD at 64 x 128 each would read 12 KB for the same
+// work, and the CU's LDS would then run at its limit).  The operands go from
+// memory straight into LDS (buffer loads with the lds bit: no registers, no
+// LDS store instructions), into a ring of five stages of 32 k each, issued
+// four stages ahead.  Each stage is a separate LDS array and the barriers
+// carry no memory fence, so the compiler's wait counts track each stage's
+// loads on their own and never drain the ring; every stage's own loads are
+// awaited by hand (vmcnt) before the barrier that publishes it.
+constexpr int kDK = 32;                  // k per stage
+constexpr int kDRows = 256;              // tile rows of each operand
+constexpr int kDStage = 2 * kDRows * kDK / 8;   // 16-byte chunks: A then B
+constexpr int kDLoads = 8;               // DMA instructions per thread per stage
+constexpr int kNSt = 5;                  // stages in the ring
+// tiles in groups of kGroupM token blocks (columns vary between groups):
+// the 32 tiles an XCD runs at once span 4 token and 8 column blocks, so its
+// L2 serves 12 operand slices per k stage (18 in token-block-first order)
+constexpr uint32_t kGroupM = 4;
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima): a stage waits for its successor with kNSt - 2
+// later stages in flight; the prologue waits for stage 0 of kNSt
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitStage = vmcnt_imm((kNSt - 2) * kDLoads);
+constexpr int kWaitPrologue = vmcnt_imm((kNSt - 1) * kDLoads);
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer resource (voff per lane, soff per wave)
+// into LDS at lds + 16 lane (lds wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t res, u32x4 *lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void *)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+// LDS layout of a stage: operand row r (of 256; A rows, then B rows) is 4
+// chunks of 16 bytes (32 k), logical chunk j stored at position
+// j ^ ((r / 4) % 4): the 16 consecutive rows that one operand read touches
+// at one logical chunk land in 16 distinct bank groups.
+
+template <int R, bool kFp8>
+__global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a) {
+    constexpr int WM = 2, WN = 2, TI = 4, kBM = kDRows;
+    // the ring; after the main loop stages 0-3 hold the finished tile and
+    // stage 4 the tile's cos/sin rows
+    __shared__ u32x4 st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage], st4[kDStage];
+    static_assert(kBM * 64 * 2 <= kDStage * 16, "cos/sin rows fit one stage");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv % WM;
+    const int wn = wv / WM;
+    const uint32_t mblocks = (a.num_ctx + kBM - 1) / kBM;
+    uint32_t bid = blockIdx.x;
+    const uint32_t full = gridDim.x - gridDim.x % kPNumXcds;
+    if (bid < full) bid = (bid % kPNumXcds) * (full / kPNumXcds) + bid / kPNumXcds;
+    // workgroup i runs on XCD i % 8: XCD x takes a contiguous run of the
+    // grouped tile order
+    const uint32_t nblocks = a.cols / (128 * WN);
+    const uint32_t gsz = kGroupM * nblocks;
+    const uint32_t gm0 = (bid / gsz) * kGroupM;
+    const uint32_t gm = mblocks - gm0 < kGroupM ? mblocks - gm0 : kGroupM;
+    const uint32_t rem = bid % gsz;
+    const uint32_t mb = gm0 + rem % gm;
+    const uint32_t nb = rem / gm;
+    const int64_t m0 = static_cast<int64_t>(mb) * kBM;
+    const int64_t n0 = static_cast<int64_t>(nb) * (128 * WN);
+
+    // DMA roles: instruction p of wave wv fills rows 64 p + 16 wv .. + 15 of
+    // an operand (1 KB of LDS, 16 bytes per lane in lane order); lane l holds
+    // physical chunk l % 4 of row 16 wv + l / 4, i.e. logical chunk
+    // (l % 4) ^ ((l / 16) % 4).  Rows past num_ctx read as zero.
+    const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.z), 0, static_cast<int>(a.num_ctx * 2u * a.hidden), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.W), 0, static_cast<int>(a.cols * 2u * a.hidden), 0x00020000);
+    const int row_bytes = 2 * a.hidden;
+    const int drow = 16 * wv + (lane >> 2);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const int zoff = (static_cast<int>(m0) + drow) * row_bytes + dchunk * 16;
+    const int woff = (static_cast<int>(n0) + drow) * row_bytes + dchunk * 16;
+    const int pstep = 64 * row_bytes;
+    const int nk = a.hidden / kDK;
+    auto issue = [&](u32x4 *st, int kt) {
+        const int ko = kt * (kDK * 2);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            dma16(zres, st + (64 * p + 16 * wv) * 4, zoff, p * pstep + ko);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            dma16(wres, st + kDRows * 4 + (64 * p + 16 * wv) * 4, woff, p * pstep + ko);
+    };
+
+    // operand reads: rows wrow + 32 i + cl of A and 128 wn + 32 n + cl of B,
+    // logical chunk 2 s + hi of the k step s (0, 1) of a stage
+    const int hi = lane >> 5;
+    const int cl = lane & 31;
+    const int wrow = 32 * TI * wm;
+    const int arow = (wrow + cl) * 4;
+    const int brow = kDRows * 4 + (128 * wn + cl) * 4;
+    const int xs0 = hi ^ ((cl >> 2) & 3);
+    const int xs1 = (2 + hi) ^ ((cl >> 2) & 3);
+
+    int64_t my_pos = 0;
+    if (tid < kBM) {
+        int64_t t = m0 + tid;
+        if (t >= a.num_ctx) t = a.num_ctx - 1;
+        my_pos = a.positions[t];
+    }
+    int64_t my_slot[TI / 2];
+#pragma unroll
+    for (int u = 0; u < TI / 2; ++u) {
+        const int64_t t = m0 + wrow + 64 * u + lane;
+        my_slot[u] = t < a.num_ctx ? a.slots[t] : -1;
+    }
+
+    f32x16 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = f32x16{};
+
+    bf16x8 fa[2][TI], fb[2][4];
+    auto read_frags = [&](int buf, const u32x4 *st, int xs) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+            fa[buf][i] = __builtin_bit_cast(bf16x8, st[arow + 128 * i + xs]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            fb[buf][n] = __builtin_bit_cast(bf16x8, st[brow + 128 * n + xs]);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][n], fa[buf][i],
+                                                                    acc[i][n], 0, 0, 0);
+    };
+    // Instruction schedule of a k step: the next step's LDS operand reads
+    // (and, after a barrier, the stage's loads) go out between the first
+    // MFMAs, so that their latency is behind the remaining ones.
+    // sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int g = 0; g < TI + 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TI - TI - 4, 0);
+    };
+    auto interleave_loads = [&]() {
+#pragma unroll
+        for (int g = 0; g < TI + 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TI - TI - 4, 0);
+    };
+    // Stage kt (array cur, the next stage's array nxt): the MFMAs of k step
+    // 0 run while step 1's operands are read; then this wave's loads of
+    // stage kt + 1 are awaited (kNSt - 2 later stages may still be in
+    // flight), its LDS reads drained, and the barrier publishes stage kt + 1
+    // and retires stage kt, which is refilled at once with stage kt + 5
+    // (clamped to the last stage: the ring's tail reloads what it holds, so
+    // that every stage issues the same number of loads); the MFMAs of step 1
+    // run while step 0 of stage kt + 1 is read.
+    auto stage = [&](u32x4 *cur, u32x4 *nxt, int kt) {
+        read_frags(1, cur, xs1);
+        mfmas(0);
+        interleave();
+        __builtin_amdgcn_s_waitcnt(kWaitStage);
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        issue(cur, kt + kNSt < nk ? kt + kNSt : nk - 1);
+        read_frags(0, nxt, xs0);
+        mfmas(1);
+        interleave_loads();
+    };
+
+    // prologue: the first kNSt stages (clamped), then stage 0 awaited
+    u32x4 *const stp[5] = {st0, st1, st2, st3, st4};
+#pragma unroll
+    for (int j = 0; j < kNSt; ++j) issue(stp[j], j < nk ? j : nk - 1);
+    __builtin_amdgcn_s_waitcnt(kWaitPrologue);
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, st0, xs0);
+    int kt = 0;
+    for (; kt + kNSt <= nk; kt += kNSt) {
+#pragma unroll
+        for (int j = 0; j < kNSt; ++j) stage(stp[j], stp[(j + 1) % kNSt], kt + j);
+    }
+    // the last nk % kNSt stages start the ring again at stage array 0
+#pragma unroll
+    for (int j = 0; j < kNSt - 1; ++j)
+        if (kt + j < nk) stage(stp[j], stp[j + 1], kt + j);
+    // every load (the tail's reloads too) has landed before the stages are
+    // reused for the finished tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
+    __syncthreads();
+
+    project_epilogue<R, kFp8, WM, WN, TI, kBM>(
+        a, acc, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(st4),
+        [&](int row) {
+            constexpr int kRowBytes = kFp8 ? 128 : 256;
+            constexpr int kRowsPerStage = kDStage * 16 / kRowBytes;
+            const int q = row / kRowsPerStage;
+            u32x4 *base = q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
+            return reinterpret_cast<uint8_t *>(base) + (row % kRowsPerStage) * kRowBytes;
+        });
+}
 
 template <int R, bool kFp8>
 void launch_pw(const ProjArgs &a, hipStream_t stream) {
-    using T = Tile<kWM, kWN, kTI>;
-    const uint32_t mblocks = (a.num_ctx + T::kBM - 1) / T::kBM;
-    hipLaunchKernelGGL((project_write_kernel<R, kFp8, kWM, kWN, kTI, kDepth>),
-                       dim3(mblocks * (a.cols / T::kBN)), dim3(T::kThreads), 0, stream, a);
+    const uint32_t mblocks = (a.num_ctx + kDRows - 1) / kDRows;
+    hipLaunchKernelGGL((project_write_kernel<R, kFp8>), dim3(mblocks * (a.cols / 256)), dim3(256),
+                       0, stream, a);
 }
 
 }  // namespace

@@ -95,6 +95,9 @@ EXACT_SWEEP = [
     (256, 1024, 3, 2, 64, 64, 8, False, 0.5),
     (1000, 128, 1, 8, 32, 128, 8, True, 0.05),
     (700, 2048, 2, 4, 64, 16, 64, False, 0.02),
+    # k in whole rings of five 32-wide stages, no tail
+    (200, 320, 2, 2, 32, 16, 32, False, 0.1),
+    (333, 960, 1, 4, 16, 8, 64, True, 0.1),
 ]
 
 
