@@ -576,6 +576,12 @@ def main():
                              "timing": "%d writes as HIP-graph replays (50 writes per graph)"
                                        % r["calls"],
                              "bytes_per_call": r["bytes"]}
+            # a plain copy of the same byte volume under the same replay (one
+            # buffer pair, as the write reuses one input set): the practical
+            # ceiling of a launch this small
+            ref = small_copy_reference(r["bytes"], 1, stream, per_graph=50)
+            results[name]["same_size_copy"] = ref
+            results[name]["pct_of_same_size_copy"] = 100.0 * results[name]["GB_s"] / ref["GB_s"]
         else:
             n_sets = 1 if index == 3 else args.sets
             setup = Setup(index, n_sets, dev)

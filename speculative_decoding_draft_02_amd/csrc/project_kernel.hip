@@ -40,9 +40,60 @@ namespace {
 
 // ------------------------------------------------------------ hidden norm --
 
-// One wave per row: the sum of squares over the row (bf16 dot2, DPP row sums,
-// then the four 16-lane partials added in a fixed order), then the row again
-// (from L2) for y = (x r)(1 + w) rounded to bf16.
+// One wave per row: the sum of squares over the row (each lane adds its
+// chunks c = lane, lane + 64, ... in that order with bf16 dot2, then DPP row
+// sums and the four 16-lane partials added in a fixed order), then
+// y = (x r)(1 + w) rounded to bf16.  Rows of up to 64 kPer chunks stay in
+// registers between the two steps (one read of the row); longer rows are read
+// again (from L2).  Both give the same sums in the same order.
+constexpr int kNormPer = 16;    // chunks per lane held in registers: dim <= 8192
+
+__global__ __launch_bounds__(256) void hidden_norm_resident_kernel(
+    const uint16_t *x, const uint16_t *w, uint16_t *out, uint32_t rows, int32_t dim, float eps) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t row = blockIdx.x * 4 +
+                         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    if (row >= rows) return;
+    const int chunks = dim / 8;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<int64_t>(row) * dim);
+    uint4 d[kNormPer];
+#pragma unroll
+    for (int j = 0; j < kNormPer; ++j)
+        if (64 * j < chunks) d[j] = lane + 64 * j < chunks ? load_row16(xr + lane + 64 * j)
+                                                           : make_uint4(0, 0, 0, 0);
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kNormPer; ++j)
+        if (64 * j < chunks && lane + 64 * j < chunks) {
+            ss = dot2_bf16(d[j].x, d[j].x, ss);
+            ss = dot2_bf16(d[j].y, d[j].y, ss);
+            ss = dot2_bf16(d[j].z, d[j].z, ss);
+            ss = dot2_bf16(d[j].w, d[j].w, ss);
+        }
+    ss = row_sum16(ss);
+    ss = lane_value(ss, 0) + lane_value(ss, 16) + lane_value(ss, 32) + lane_value(ss, 48);
+    const float r = __builtin_amdgcn_rsqf(ss / static_cast<float>(dim) + eps);
+    const uint4 *wr = reinterpret_cast<const uint4 *>(w);
+    uint4 *orow = reinterpret_cast<uint4 *>(out + static_cast<int64_t>(row) * dim);
+#pragma unroll
+    for (int j = 0; j < kNormPer; ++j) {
+        const int c = lane + 64 * j;
+        if (64 * j < chunks && c < chunks) {
+            const uint4 wv = wr[c];
+            const uint32_t dw[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float x0 = bf16_lo(dw[k]) * r, x1 = bf16_hi(dw[k]) * r;
+                o[k] = pack_bf16(__builtin_fmaf(x0, bf16_lo(ww[k]), x0),
+                                 __builtin_fmaf(x1, bf16_hi(ww[k]), x1));
+            }
+            store_row16(orow + c, make_uint4(o[0], o[1], o[2], o[3]));
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void hidden_norm_kernel(const uint16_t *x, const uint16_t *w,
                                                           uint16_t *out, uint32_t rows,
                                                           int32_t dim, float eps) {
@@ -476,8 +527,12 @@ void launch_pw(const ProjArgs &a, hipStream_t stream) {
 
 hipError_t launch_hidden_norm(const uint16_t *x, const uint16_t *w, uint16_t *out, uint32_t rows,
                               int32_t dim, float eps, hipStream_t stream) {
-    hipLaunchKernelGGL(hidden_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, w, out,
-                       rows, dim, eps);
+    if (dim <= 8 * 64 * kNormPer)
+        hipLaunchKernelGGL(hidden_norm_resident_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
+                           x, w, out, rows, dim, eps);
+    else
+        hipLaunchKernelGGL(hidden_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, w,
+                           out, rows, dim, eps);
     return hipGetLastError();
 }
 
