@@ -118,6 +118,8 @@ SWEEP = [
     (448, 8, 2, 64, 64, 16, True, True, True, 0.02),   # a tensor-parallel shard's heads
     (2048, 32, 8, 64, 64, 64, True, True, True, 0.05),  # 256 requests' draft rows
     (1001, 7, 1, 16, 128, 16, False, False, True, 0.3),  # 9 heads per token
+    (20, 128, 16, 64, 16, 8, True, True, True, 0.1),   # 160 heads per token
+    (50, 4, 2, 32, 2048, 1, False, True, True, 0.1),   # 2048-token blocks
 ]
 
 

@@ -85,6 +85,34 @@ def test_sweep_parity(oracle_lib, shape):
     _check(oracle_lib, wl, reverse=(L % 2 == 1))
 
 
+# the largest supported shapes: DSPARK_MAX_LAYERS layers (one wave per
+# layer, and whole row groups per wave in chunks of 8 layers), many kv heads,
+# a large block
+MAX_CASES = [
+    # N, L, nkv, R, bs, blocks, fp8, pad
+    (40, 32, 2, 64, 16, 4, False, 0.1),     # per-layer split
+    (40, 32, 2, 32, 16, 4, True, 0.1),
+    (1600, 32, 4, 16, 64, 32, False, 0.05),  # 1600 waves: chunked, not split
+    (50, 2, 64, 64, 16, 8, True, 0.1),      # 64 kv heads
+    (300, 2, 2, 32, 2048, 2, False, 0.1),   # 2048-token blocks
+]
+
+
+@pytest.mark.parametrize("shape", MAX_CASES, ids=lambda s: "N%d-L%d-H%d-R%d-bs%d-%s" % (
+    s[0], s[1], s[2], s[3], s[4], "fp8" if s[6] else "bf16"))
+def test_maximum_shapes(oracle_lib, shape):
+    N, L, nkv, R, bs, nb, fp8, pad = shape
+    wl = W.custom(N, L, nkv, R, bs, nb, fp8, seed=N + L + nkv, pad_fraction=pad,
+                  kv_std=4.0 if fp8 else 1.0)
+    _check(oracle_lib, wl, reverse=(L == 32), label="max")
+
+
+def test_maximum_layers_with_per_layer_slots(oracle_lib):
+    wl = W.custom(200, 32, 2, 32, 16, 32, True, seed=12, pad_fraction=0.05, kv_std=4.0)
+    wl = W.per_layer_slots(wl, seed=13, pad_fraction=0.1)
+    _check(oracle_lib, wl, label="max-layer-slots")
+
+
 def test_layers_allocated_in_reverse_order(oracle_lib):
     """Negative per-layer cache offsets (layer 0 allocated last)."""
     wl = W.custom(200, 5, 4, 64, 16, 64, False, seed=5, pad_fraction=0.1)

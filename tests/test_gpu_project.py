@@ -98,6 +98,8 @@ EXACT_SWEEP = [
     # k in whole rings of five 32-wide stages, no tail
     (200, 320, 2, 2, 32, 16, 32, False, 0.1),
     (333, 960, 1, 4, 16, 8, 64, True, 0.1),
+    # the largest layer count: 32 layers x 2 kinds x 1 head = 64 heads
+    (300, 128, 32, 1, 64, 16, 32, False, 0.1),
 ]
 
 
