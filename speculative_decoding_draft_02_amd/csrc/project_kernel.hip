@@ -322,11 +322,13 @@ constexpr int kNSt = 5;                  // stages in the ring
 // L2 serves 12 operand slices per k stage (18 in token-block-first order)
 constexpr uint32_t kGroupM = 4;
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
-// left at their maxima): a stage waits for its successor with kNSt - 2
-// later stages in flight; the prologue waits for stage 0 of kNSt
+// left at their maxima).  A stage's loads go out in two halves of kDLoads / 2
+// (token rows, then weight rows a half stage later); a stage waits for its
+// successor with the loads of kNSt - 2 later stages in flight, the prologue
+// for stage 0 with kNSt - 2 later stages and one half in flight.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitStage = vmcnt_imm((kNSt - 2) * kDLoads);
-constexpr int kWaitPrologue = vmcnt_imm((kNSt - 1) * kDLoads);
+constexpr int kWaitPrologue = vmcnt_imm((kNSt - 2) * kDLoads + kDLoads / 2);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -386,11 +388,14 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
     const int woff = (static_cast<int>(n0) + drow) * row_bytes + dchunk * 16;
     const int pstep = 64 * row_bytes;
     const int nk = a.hidden / kDK;
-    auto issue = [&](u32x4 *st, int kt) {
+    auto issue_a = [&](u32x4 *st, int kt) {
         const int ko = kt * (kDK * 2);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             dma16(zres, st + (64 * p + 16 * wv) * 4, zoff, p * pstep + ko);
+    };
+    auto issue_b = [&](u32x4 *st, int kt) {
+        const int ko = kt * (kDK * 2);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             dma16(wres, st + kDRows * 4 + (64 * p + 16 * wv) * 4, woff, p * pstep + ko);
@@ -442,64 +447,70 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
                 acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][n], fa[buf][i],
                                                                     acc[i][n], 0, 0, 0);
     };
-    // Instruction schedule of a k step: the next step's LDS operand reads
-    // (and, after a barrier, the stage's loads) go out between the first
-    // MFMAs, so that their latency is behind the remaining ones.
-    // sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read.
-    auto interleave = [&]() {
+    // Instruction schedule of a half stage (one 16-wide k step): 16 MFMAs
+    // with the next step's 8 LDS operand reads and 4 of the loads in between,
+    // per group of four MFMAs two reads and one load, so that their latency
+    // and issue sit behind the MFMAs.  sched_group_barrier masks: 0x008 MFMA,
+    // 0x020 VMEM read, 0x100 LDS read.
+    auto interleave_half = [&]() {
 #pragma unroll
-        for (int g = 0; g < TI + 4; ++g) {
+        for (int g = 0; g < 4; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TI - TI - 4, 0);
-    };
-    auto interleave_loads = [&]() {
-#pragma unroll
-        for (int g = 0; g < TI + 4; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TI - TI - 4, 0);
     };
-    // Stage kt (array cur, the next stage's array nxt): the MFMAs of k step
-    // 0 run while step 1's operands are read; then this wave's loads of
-    // stage kt + 1 are awaited (kNSt - 2 later stages may still be in
-    // flight), its LDS reads drained, and the barrier publishes stage kt + 1
-    // and retires stage kt, which is refilled at once with stage kt + 5
-    // (clamped to the last stage: the ring's tail reloads what it holds, so
-    // that every stage issues the same number of loads); the MFMAs of step 1
-    // run while step 0 of stage kt + 1 is read.
-    auto stage = [&](u32x4 *cur, u32x4 *nxt, int kt) {
+    // Stage kt (array cur; prev holds stage kt - 1, nxt stage kt + 1):
+    // the MFMAs of k step 0 run while step 1's operands are read and the
+    // weight half of stage kt + 4 goes into prev (retired at the last
+    // barrier); then this wave's loads of stage kt + 1 are awaited (three
+    // later stages may still be in flight), its LDS reads drained, and the
+    // barrier publishes stage kt + 1 and retires stage kt, whose refill with
+    // stage kt + 5 starts with its token half while the MFMAs of step 1 run
+    // and step 0 of stage kt + 1 is read.  Refills past the last stage load
+    // the last stage again (clamped), so that every stage issues the same
+    // number of loads and the hand-written wait counts stay exact.
+    auto clamp = [&](int k) { return k < nk ? k : nk - 1; };
+    auto stage = [&](u32x4 *prev, u32x4 *cur, u32x4 *nxt, int kt) {
         read_frags(1, cur, xs1);
+        issue_b(prev, clamp(kt + kNSt - 1));
         mfmas(0);
-        interleave();
+        interleave_half();
         __builtin_amdgcn_s_waitcnt(kWaitStage);
         __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        issue(cur, kt + kNSt < nk ? kt + kNSt : nk - 1);
+        issue_a(cur, clamp(kt + kNSt));
         read_frags(0, nxt, xs0);
         mfmas(1);
-        interleave_loads();
+        interleave_half();
     };
 
-    // prologue: the first kNSt stages (clamped), then stage 0 awaited
+    // prologue: the first kNSt - 1 stages and the token half of the last
+    // (its weight half goes out in stage 0), then stage 0 awaited
     u32x4 *const stp[5] = {st0, st1, st2, st3, st4};
 #pragma unroll
-    for (int j = 0; j < kNSt; ++j) issue(stp[j], j < nk ? j : nk - 1);
+    for (int j = 0; j < kNSt - 1; ++j) {
+        issue_a(stp[j], clamp(j));
+        issue_b(stp[j], clamp(j));
+    }
+    issue_a(stp[kNSt - 1], clamp(kNSt - 1));
     __builtin_amdgcn_s_waitcnt(kWaitPrologue);
     __builtin_amdgcn_s_barrier();
     read_frags(0, st0, xs0);
     int kt = 0;
     for (; kt + kNSt <= nk; kt += kNSt) {
 #pragma unroll
-        for (int j = 0; j < kNSt; ++j) stage(stp[j], stp[(j + 1) % kNSt], kt + j);
+        for (int j = 0; j < kNSt; ++j)
+            stage(stp[(j + kNSt - 1) % kNSt], stp[j], stp[(j + 1) % kNSt], kt + j);
     }
     // the last nk % kNSt stages start the ring again at stage array 0
 #pragma unroll
     for (int j = 0; j < kNSt - 1; ++j)
-        if (kt + j < nk) stage(stp[j], stp[j + 1], kt + j);
+        if (kt + j < nk) stage(stp[(j + kNSt - 1) % kNSt], stp[j], stp[j + 1], kt + j);
     // every load (the tail's reloads too) has landed before the stages are
     // reused for the finished tile
     __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
