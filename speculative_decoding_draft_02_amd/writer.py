@@ -279,6 +279,10 @@ class DSparkContextKVWriter:
         if num_ctx == 0:
             return
         self._ensure_tables()
+        if self._debug_checks:
+            c0 = self._layers[0].kv_cache
+            check_write_preconditions(positions, slot_mapping, cos_sin_cache.shape[0],
+                                      c0.shape[0], c0.shape[2])
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = _lib.dspark_ctx_kv_writer_project_write(
             self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(), L, nkv,

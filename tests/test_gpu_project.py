@@ -269,3 +269,29 @@ def test_project_write_graph_capture(oracle_lib):
         got = [_codes(a.kv_cache) for a in layers]
         assert C.compare(got, ref, ww.slot_mapping, True, ww.sentinel).failures == 0, rep
     writer.close()
+
+
+def test_project_write_debug_checks(oracle_lib):
+    """With debug_checks the projection refuses a slot outside the cache
+    before any launch; valid inputs write as usual."""
+    wl = W.project_exact(100, 128, 1, 2, 32, 16, 8, False, seed=3, pad_fraction=0.1)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers, debug_checks=True)
+    args = [_bf16(wl.states), _bf16(wl.kv_weight), _bf16(wl.k_norm_weight), wl.eps,
+            torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), 32]
+    slots = torch.from_numpy(wl.slot_mapping).to(DEV)
+    bad = slots.clone()
+    bad[int(torch.nonzero(bad >= 0)[0])] = wl.num_blocks * wl.block_size
+    with pytest.raises(ValueError, match="num_blocks"):
+        writer.project_write(*args, bad)
+    torch.cuda.synchronize()
+    assert all(bool((_codes(a.kv_cache) == 0xFFFF).all()) for a in layers)
+    writer.project_write(*args, slots)
+    torch.cuda.synchronize()
+    got = [_codes(a.kv_cache) for a in layers]
+    ww = wl.write_workload(oracle_lib.kv_project(wl.states, wl.kv_weight))
+    ref = oracle_lib.ctx_kv_write(ww.all_kv, ww.k_norm_weight, ww.eps, ww.positions, ww.cos_sin,
+                                  32, ww.slot_mapping, ww.new_host_caches(), False,
+                                  ww.k_scales, ww.v_scales)
+    assert C.compare(got, ref, ww.slot_mapping, False, ww.sentinel).failures == 0
+    writer.close()
