@@ -349,6 +349,23 @@ def time_unfused(setup: UnfusedSetup, steps: int, warmup: int, stream):
     return start.elapsed_time(end) * 1e-3 / steps
 
 
+def count_device_ops(fn, stream):
+    """Device operations (kernels, copies, fills) one call of fn puts on the
+    GPU, counted with torch's profiler outside any timed region; None if the
+    profiler is unavailable."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            with profile(activities=[ProfilerActivity.CUDA]) as prof:
+                fn()
+                torch.cuda.synchronize()
+        return sum(1 for e in prof.events()
+                   if e.device_type == torch.autograd.DeviceType.CUDA)
+    except Exception:   # profiler support differs between builds: report nothing
+        return None
+
+
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
@@ -609,13 +626,18 @@ def main():
         results[name]["pct_of_hbm_peak"] = 100.0 * results[name].get("kernel_GB_s", results[name]["GB_s"]) / HBM_PEAK_GBS
         if not args.no_unfused:
             # the base path the fused write replaces, on the same inputs and caches
-            ut = time_unfused(UnfusedSetup(setup, dev), min(args.steps, 50), 3, stream)
+            us = UnfusedSetup(setup, dev)
+            ut = time_unfused(us, min(args.steps, 50), 3, stream)
+            unfused_ops = count_device_ops(lambda: us.launch(0, None), stream)
+            fused_ops = count_device_ops(lambda: setup.launch(0, stream.cuda_stream), stream)
             fused_us = results[name].get("kernel_us_avg", results[name].get("us_per_call"))
             results[name]["unfused_torch"] = {
                 "us_per_call": ut * 1e6, "speedup_of_fused": ut * 1e6 / fused_us,
                 "how": "permute copy, per-layer Gemma K norm + stack, positions.repeat, NeoX "
                        "rotary, per-layer cache write, in PyTorch ops (one host sync per call "
-                       "for the valid-token list); eager, %d calls" % min(args.steps, 50)}
+                       "for the valid-token list); eager, %d calls" % min(args.steps, 50),
+                "device_ops_per_call": unfused_ops,
+                "fused_device_ops_per_call": fused_ops}
         log(name, json.dumps(results[name]))
         del setup
         torch.cuda.empty_cache()
