@@ -111,6 +111,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
 
     uint32_t t;
     int h;
+    int hu = 0;                     // uniform path: the head of quarter 0
     int64_t slot, pos;
     uint4 dk[kChunk], dv[kChunk], wv[kChunk];
     int64_t lslot[kChunk];          // per-layer slots (kLayerSlots only)
@@ -132,7 +133,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     };
     if constexpr (kUniform) {
         t = unit0 / static_cast<uint32_t>(nkv);
-        h = static_cast<int>(unit0 - t * static_cast<uint32_t>(nkv)) + q;
+        hu = static_cast<int>(unit0 - t * static_cast<uint32_t>(nkv));
+        h = hu + q;
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
                   ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         slot = a.slots[t];
@@ -195,6 +197,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     const int64_t off = slot & ((int64_t{1} << a.bs_log2) - 1);
     // element index of this row inside any layer's cache, plus this lane's chunk
     const int64_t row = ((((blk * nkv + h) << a.bs_log2) + off) * (2 * DSPARK_HEAD_DIM)) + c * 8;
+    // uniform path: quarter q's row lies (q << bs_log2) rows after quarter 0's,
+    // whose address is the same for the whole wave, so the stores go through
+    // a buffer resource on that address with the sc1 policy (lane offsets
+    // below 2^31 bytes while block_size <= 2^20)
+    const int64_t row0 = (((blk * nkv + hu) << a.bs_log2) + off) * (2 * DSPARK_HEAD_DIM);
+    const uint32_t lane_elem =
+        (static_cast<uint32_t>(q) << a.bs_log2) * (2 * DSPARK_HEAD_DIM) + static_cast<uint32_t>(c) * 8;
+    const bool sc1 = !kUniform || a.bs_log2 <= 20;   // the other paths check per layer
 
     for (int lb = 0;;) {
         // fp8: lane 2j holds layer lb+j's k scale, lane 2j+1 its v scale, and
@@ -219,21 +229,65 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             if (l >= L) break;
             uint32_t kb[4];
             norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb);
-            int64_t base = a.cache_off[l0 + l] + row;
+            // element index of this lane's row start (chunk excluded) in layer l
+            int64_t rbase = a.cache_off[l0 + l] + row - c * 8;
             bool store = true;
             if constexpr (kLayerSlots) {
                 const int64_t s = lslot[j];
                 store = in_range && s >= 0;
                 const int64_t lb_blk = s >> a.bs_log2;
                 const int64_t lb_off = s & ((int64_t{1} << a.bs_log2) - 1);
-                base = a.cache_off[l] +
-                       ((((lb_blk * nkv + h) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM)) + c * 8;
+                rbase = a.cache_off[l] +
+                        ((((lb_blk * nkv + h) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM));
             }
+            // the stores go through a buffer resource on a wave-uniform base
+            // with the sc1 policy when every lane's offset fits in 31 bits,
+            // else as nontemporal stores to the lane's address
+            constexpr int kEsz = kFp8 ? 1 : 2;
+            bool use_sc1 = sc1;
+            __amdgpu_buffer_rsrc_t r;
+            uint32_t loff;
+            if constexpr (kUniform) {
+                r = wave_rsrc(static_cast<char *>(a.cache0) + (a.cache_off[l0 + l] + row0) * kEsz);
+                loff = lane_elem * kEsz;
+            } else if constexpr (!kLayerSlots) {
+                // the general row mapping (quarters of different tokens, nkv
+                // not a multiple of 4) measured slower with sc1 stores (the
+                // 4096-token prefill at nkv = 2: 10.2 vs 9.3 us)
+                use_sc1 = false;
+                r = wave_rsrc(a.cache0);
+                loff = 0;
+            } else {
+                // per-layer slots: the base is the lowest of the four row
+                // starts (a row this layer does not store takes the first
+                // stored one's address)
+                int64_t qa = reinterpret_cast<int64_t>(static_cast<char *>(a.cache0) + rbase * kEsz);
+                const uint64_t sm = __ballot(store);
+                if (sm == 0) continue;
+                if (!store) qa = read_lane64(qa, static_cast<int>(__builtin_ctzll(sm)));
+                const int64_t a0 = read_lane64(qa, 0), a1 = read_lane64(qa, 16);
+                const int64_t a2 = read_lane64(qa, 32), a3 = read_lane64(qa, 48);
+                const int64_t lo = a0 < a1 ? (a0 < a2 ? (a0 < a3 ? a0 : a3) : (a2 < a3 ? a2 : a3))
+                                           : (a1 < a2 ? (a1 < a3 ? a1 : a3) : (a2 < a3 ? a2 : a3));
+                const int64_t hi = a0 > a1 ? (a0 > a2 ? (a0 > a3 ? a0 : a3) : (a2 > a3 ? a2 : a3))
+                                           : (a1 > a2 ? (a1 > a3 ? a1 : a3) : (a2 > a3 ? a2 : a3));
+                use_sc1 = hi - lo < (int64_t{1} << 31) - 1024;
+                r = wave_rsrc(reinterpret_cast<void *>(lo));
+                loff = static_cast<uint32_t>(qa - lo) + static_cast<uint32_t>(c) * 8 * kEsz;
+            }
+            const int64_t base = rbase + c * 8;
             if constexpr (!kFp8) {
-                uint16_t *cache = static_cast<uint16_t *>(a.cache0) + base;
-                if (store) {
-                    store_row16(cache, make_uint4(kb[0], kb[1], kb[2], kb[3]));
-                    store_row16(cache + DSPARK_HEAD_DIM, dv[j]);
+                if (use_sc1) {
+                    if (store) {
+                        store16_sc1(r, loff, make_uint4(kb[0], kb[1], kb[2], kb[3]));
+                        store16_sc1(r, loff + DSPARK_HEAD_DIM * 2, dv[j]);
+                    }
+                } else {
+                    uint16_t *cache = static_cast<uint16_t *>(a.cache0) + base;
+                    if (store) {
+                        store_row16(cache, make_uint4(kb[0], kb[1], kb[2], kb[3]));
+                        store_row16(cache + DSPARK_HEAD_DIM, dv[j]);
+                    }
                 }
             } else {
                 const float ks = lane_value(my_scale, 2 * j), kr = lane_value(my_rcp, 2 * j);
@@ -241,10 +295,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                 const uint32_t vb[4] = {dv[j].x, dv[j].y, dv[j].z, dv[j].w};
                 const uint2 ko = pack_fp8(kb, ks, kr, 460.0f * ks);
                 const uint2 vo = pack_fp8(vb, vs, vr, 460.0f * vs);
-                uint8_t *cache = static_cast<uint8_t *>(a.cache0) + base;
-                if (store) {
-                    store_row8(cache, ko);
-                    store_row8(cache + DSPARK_HEAD_DIM, vo);
+                if (use_sc1) {
+                    if (store) {
+                        store8_sc1(r, loff, ko);
+                        store8_sc1(r, loff + DSPARK_HEAD_DIM, vo);
+                    }
+                } else {
+                    uint8_t *cache = static_cast<uint8_t *>(a.cache0) + base;
+                    if (store) {
+                        store_row8(cache, ko);
+                        store_row8(cache + DSPARK_HEAD_DIM, vo);
+                    }
                 }
             }
         }

@@ -88,6 +88,34 @@ __device__ __forceinline__ void store_row8(void *p, const uint2 &v) {
     }
 }
 
+// Stores with the sc1 cache policy (device scope) through a buffer resource
+// whose base is a wave-uniform address: the lanes add byte offsets below
+// 2^31.  On the write's scattered rows this measured 9% more HBM throughput
+// than nontemporal stores (a copy of the same address pattern: 6.1 vs 5.6
+// TB/s).  The resource has no range limit: offsets are the caller's to bound.
+constexpr int kStoreSc1 = 16;   // cache-policy bit sc1 of a buffer store
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *wave_base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(wave_base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+    const uint32_t hi =
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+    void *p = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, -1, 0x00020000);
+}
+
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                            const uint4 &v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(byte_off), 0, kStoreSc1);
+}
+
+__device__ __forceinline__ void store8_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                           const uint2 &v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(byte_off), 0, kStoreSc1);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
