@@ -35,7 +35,11 @@
 //     rounded quotient for every finite bf16 x at the e4m3 resolution
 //     (Markstein's correction step) on x clamped to +-460 scale, which also
 //     keeps the result inside the e4m3 range; then the hardware pack
-//     conversion v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950).
+//     conversion v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950);
+//   * loads are nontemporal; the cache stores carry the sc1 policy through a
+//     buffer resource on a wave-uniform base (uniform-token rows and
+//     per-layer slots), which moves the scattered 512-byte rows faster than
+//     nontemporal stores; the general row mapping keeps nontemporal stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -12,8 +12,10 @@
 namespace dspark {
 namespace {
 
-// Cache policy of the streams: all_kv is read once and the cache rows are
-// written once, so both go through the nontemporal (streaming) path.
+// Cache policy of the streams: inputs are read once and go through the
+// nontemporal (streaming) path; so do the stores of store_row16/store_row8
+// (the context write's scattered cache rows use the sc1 stores below where
+// it can).
 constexpr bool kStreamLoads = true;
 constexpr bool kStreamStores = true;
 // DPP control codes (CDNA3/CDNA4 ISA, DPP_CTRL field).
