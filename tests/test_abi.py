@@ -344,3 +344,29 @@ def test_debug_precondition_checks_on_cpu_tensors():
     chk(pos, [ok, torch.tensor([1, 2, 3, 4])], 10, 2, 4)
     with pytest.raises(ValueError, match="slot mapping 1"):
         chk(pos, [ok, torch.tensor([1, 1, 3, 4])], 10, 2, 4)
+
+
+def test_write_preconditions_on_cpu_tensors():
+    """The host-side precondition check behind debug_checks: positions inside
+    the cos/sin table, slots inside the cache, no shared slot within a
+    layer's mapping; padding (slot < 0) is exempt from all three."""
+    import torch
+    from speculative_decoding_draft_02_amd.writer import check_write_preconditions as chk
+    pos = torch.tensor([0, 5, 9, 3], dtype=torch.int64)
+    slots = torch.tensor([4, -1, 7, 0], dtype=torch.int64)
+    chk(pos, slots, cos_sin_rows=10, num_blocks=2, block_size=4)          # valid
+    chk(torch.tensor([0, 99, 9, 3]), slots, 10, 2, 4)                       # padding token's position is free
+    with pytest.raises(ValueError, match="cos/sin table"):
+        chk(torch.tensor([0, 5, 10, 3]), slots, 10, 2, 4)
+    with pytest.raises(ValueError, match="cos/sin table"):
+        chk(torch.tensor([-1, 5, 9, 3]), slots, 10, 2, 4)
+    with pytest.raises(ValueError, match="num_blocks"):
+        chk(pos, torch.tensor([4, -1, 8, 0]), 10, 2, 4)
+    with pytest.raises(ValueError, match="share a slot"):
+        chk(pos, torch.tensor([4, -1, 4, 0]), 10, 2, 4)
+    chk(pos, torch.tensor([-1, -1, -1, -1]), 10, 2, 4)                      # all padding
+    # per-layer mappings: each layer is checked on its own
+    per = [torch.tensor([4, -1, 7, 0]), torch.tensor([0, 1, 2, 3])]
+    chk(pos, per, 10, 2, 4)
+    with pytest.raises(ValueError, match="slot mapping 1"):
+        chk(pos, [per[0], torch.tensor([0, 1, 1, 3])], 10, 2, 4)
