@@ -49,11 +49,10 @@
 namespace dspark {
 namespace {
 
-// Waves per workgroup: 4, or 8 for large writes into bf16 caches (measured:
-// the larger workgroup is about 1% faster on the bf16 prefill, 5% slower on
-// the fp8 prefill, whose longer arithmetic favours finer scheduling, and
-// slower on small writes, which then spread over fewer CUs).
-constexpr int kWideBlockMinWaves = 4096;
+// Waves per workgroup: 4.  (Eight-wave workgroups were about 1% faster on
+// the bf16 prefill while its stores were nontemporal; with the sc1 stores
+// four waves are 0.8% faster, and they are faster on small and fp8 writes.)
+constexpr int kWavesPerGroup = 4;
 // Writes of at most this many 4-row waves give each layer its own wave
 // (bf16 caches, fp8 caches: the fp8 store's longer arithmetic gains up to
 // larger writes).  Measured under graph replay, L = 5: the split saves 0.7 us
@@ -360,13 +359,7 @@ void launch_one(const CtxKvArgs &a, hipStream_t stream) {
         launch_split<R, kFp8>(a, waves, stream);
         return;
     }
-    if constexpr (!kFp8) {
-        if (waves >= kWideBlockMinWaves) {
-            launch_wpb<R, kFp8, kChunk, kSinglePass, 8>(a, waves, stream);
-            return;
-        }
-    }
-    launch_wpb<R, kFp8, kChunk, kSinglePass, 4>(a, waves, stream);
+    launch_wpb<R, kFp8, kChunk, kSinglePass, kWavesPerGroup>(a, waves, stream);
 }
 
 template <int R, bool kFp8>
