@@ -396,8 +396,14 @@ class ProjectSetup:
         self.cs = bf16_dev(wl.cos_sin, dev)
         self.slots = torch.from_numpy(wl.slot_mapping).to(dev)
         self.z = torch.empty_like(self.states)
-        from speculative_decoding_draft_02_amd.project import hidden_norm
+        from speculative_decoding_draft_02_amd.project import hidden_norm, pack_kv_weight
         self._hidden_norm = hidden_norm
+        self._pack = pack_kv_weight
+        self.Wp = pack_kv_weight(self.W)
+
+    def pack(self):
+        """The one-time packing of the weight (not part of a step)."""
+        self.Wp = self._pack(self.W)
 
     def norm(self):
         self._hidden_norm(self.states, self.hw, self.wl.eps, out=self.z)
@@ -405,6 +411,11 @@ class ProjectSetup:
     def project_write(self):
         wl = self.wl
         self.writer.project_write(self.z, self.W, self.kw, wl.eps, self.pos, self.cs,
+                                  wl.rotary_dim, self.slots)
+
+    def project_write_packed(self):
+        wl = self.wl
+        self.writer.project_write(self.z, self.Wp, self.kw, wl.eps, self.pos, self.cs,
                                   wl.rotary_dim, self.slots)
 
     def unfused(self):
@@ -691,17 +702,23 @@ def main():
             # the clock settles over the first calls: warm both paths, then
             # alternate rounds of each and take the medians
             steps = max(10, min(args.steps, 20))
-            for fn in (ps.norm, ps.project_write, ps.unfused):
+            for fn in (ps.norm, ps.project_write, ps.project_write_packed, ps.unfused, ps.pack):
                 time_calls(fn, 10, 0, stream)
-            rounds = {"norm": [], "pw": [], "fused": [], "unfused": []}
+            rounds = {"norm": [], "pw": [], "pwp": [], "fused": [], "fusedp": [], "unfused": [],
+                      "pack": []}
             for _ in range(5):
                 rounds["norm"].append(time_calls(ps.norm, steps, 0, stream))
                 rounds["pw"].append(time_calls(ps.project_write, steps, 0, stream))
+                rounds["pwp"].append(time_calls(ps.project_write_packed, steps, 0, stream))
                 rounds["fused"].append(time_calls(lambda: (ps.norm(), ps.project_write()),
                                                   steps, 0, stream))
+                rounds["fusedp"].append(time_calls(lambda: (ps.norm(), ps.project_write_packed()),
+                                                   steps, 0, stream))
                 rounds["unfused"].append(time_calls(ps.unfused, steps, 0, stream))
-            t_norm, t_pw, t_fused, t_unfused = (float(np.median(rounds[k]))
-                                                for k in ("norm", "pw", "fused", "unfused"))
+                rounds["pack"].append(time_calls(ps.pack, 3, 0, stream))
+            t_norm, t_pw, t_pwp, t_fused, t_fusedp, t_unfused, t_pack = (
+                float(np.median(rounds[k]))
+                for k in ("norm", "pw", "pwp", "fused", "fusedp", "unfused", "pack"))
             wl = ps.wl
             flops = wl.gemm_flops()
             norm_bytes = 2 * wl.num_ctx * wl.hidden * 2 + wl.hidden * 2
@@ -717,6 +734,15 @@ def main():
                 "unfused_pipeline": "hidden norm, torch linear (hipBLASLt) writing all_kv, "
                                     "context write kernel",
                 "speedup_of_fused": t_unfused / t_fused,
+                "packed_weight": {
+                    "project_write_us": t_pwp * 1e6,
+                    "project_write_TFLOP_s": flops / t_pwp / 1e12,
+                    "pct_of_bf16_mfma_peak": 100.0 * flops / t_pwp / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                    "pipeline_us": t_fusedp * 1e6,
+                    "speedup_of_fused": t_unfused / t_fusedp,
+                    "weight_pack_us_once": t_pack * 1e6,
+                    "how": "the same projection from the weight packed once in the "
+                           "fragment-major layout (dspark_kv_weight_pack); same bytes written"},
                 "gemm_flops": flops,
                 "timing": "medians of 5 alternating rounds of %d calls each, after 10 "
                           "warm-up calls per path" % steps}

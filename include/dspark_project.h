@@ -61,6 +61,37 @@ int dspark_ctx_kv_writer_project_write(dspark_ctx_kv_writer *w, const void *stat
                                        int64_t cos_sin_rows, int32_t rotary_dim,
                                        const int64_t *slot_mapping, void *stream);
 
+/* The projection's weight in its fragment-major layout, for
+ * dspark_ctx_kv_writer_project_write_packed.  kv_weight is bf16 [cols, hidden]
+ * (row-major, as above); packed receives the same cols * hidden bf16
+ * values, element (c, k) at index
+ *     ((c / 32) * (hidden / 16) + k / 16) * 512 + 8 * (c % 32 + 32 * ((k % 16) / 8)) + k % 8,
+ * so that each 32 x 16 operand fragment of the matrix cores (32 output
+ * columns by 16 inputs, in the lane order the MFMA reads it) is 1 KB
+ * contiguous.  A weight is static, so it is packed once (a permutation:
+ * no arithmetic, no rounding).  cols a positive multiple of 32, hidden of
+ * 16, cols * hidden * 2 below 2^31 bytes; both buffers device memory,
+ * 16-byte aligned, not overlapping; the caller owns both.  One launch on
+ * `stream`, no allocation.  Returns DSPARK_OK, DSPARK_E_ARG or
+ * DSPARK_E_HIP. */
+int dspark_kv_weight_pack(const void *kv_weight, int64_t cols, int32_t hidden, void *packed,
+                          void *stream);
+
+/* dspark_ctx_kv_writer_project_write with the weight packed by
+ * dspark_kv_weight_pack (same hidden and cols = num_layers * 2 *
+ * num_kv_heads * 128); every other argument, precondition, return value and
+ * result as there, bit for bit: the same products are accumulated in the
+ * same order.  The kernel loads the packed weight straight into registers
+ * instead of staging it in LDS. */
+int dspark_ctx_kv_writer_project_write_packed(dspark_ctx_kv_writer *w, const void *states,
+                                              int64_t num_ctx, int32_t hidden,
+                                              const void *packed_kv_weight, int32_t num_layers,
+                                              int32_t num_kv_heads, const void *k_norm_weight,
+                                              float eps, const int64_t *positions,
+                                              const void *cos_sin_cache, int64_t cos_sin_rows,
+                                              int32_t rotary_dim, const int64_t *slot_mapping,
+                                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,10 @@ SIGNATURES = {
     "dspark_hidden_norm": ([_P, _I64, _I32, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "dspark_ctx_kv_writer_project_write": ([_P, _P, _I64, _I32, _P, _I32, _I32, _P, ctypes.c_float,
                                             _P, _P, _I64, _I32, _P, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_project_write_packed": ([_P, _P, _I64, _I32, _P, _I32, _I32, _P,
+                                                   ctypes.c_float, _P, _P, _I64, _I32, _P, _P],
+                                                  ctypes.c_int),
+    "dspark_kv_weight_pack": ([_P, _I64, _I32, _P, _P], ctypes.c_int),
     "dspark_qknorm_rope_kv_insert": ([_P, _I64, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                       ctypes.c_float, _P, _P, _I64, _I32, _I32, _P, _P, _P,
                                       ctypes.c_float, _P], ctypes.c_int),
@@ -141,3 +145,16 @@ def dspark_ctx_kv_writer_project_write(writer, states, num_ctx, hidden, kv_weigh
     return load().dspark_ctx_kv_writer_project_write(
         writer, states, num_ctx, hidden, kv_weight, num_layers, num_kv_heads, k_norm_weight, eps,
         positions, cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)
+
+
+def dspark_ctx_kv_writer_project_write_packed(writer, states, num_ctx, hidden, packed_kv_weight,
+                                              num_layers, num_kv_heads, k_norm_weight, eps,
+                                              positions, cos_sin_cache, cos_sin_rows, rotary_dim,
+                                              slot_mapping, stream) -> int:
+    return load().dspark_ctx_kv_writer_project_write_packed(
+        writer, states, num_ctx, hidden, packed_kv_weight, num_layers, num_kv_heads, k_norm_weight,
+        eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)
+
+
+def dspark_kv_weight_pack(kv_weight, cols, hidden, packed, stream) -> int:
+    return load().dspark_kv_weight_pack(kv_weight, cols, hidden, packed, stream)

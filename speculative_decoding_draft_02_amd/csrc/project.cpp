@@ -41,11 +41,15 @@ extern "C" int dspark_hidden_norm(const void *x, int64_t rows, int32_t dim, cons
     return DSPARK_OK;
 }
 
-extern "C" int dspark_ctx_kv_writer_project_write(
-    dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, int32_t hidden,
-    const void *kv_weight, int32_t num_layers, int32_t num_kv_heads, const void *k_norm_weight,
-    float eps, const int64_t *positions, const void *cos_sin_cache, int64_t cos_sin_rows,
-    int32_t rotary_dim, const int64_t *slot_mapping, void *stream) {
+namespace {
+
+// Checks and launch shared by the two projection entry points (kv_weight
+// row-major, or in the fragment-major packing).
+int project_write(dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, int32_t hidden,
+                  const void *kv_weight, int32_t num_layers, int32_t num_kv_heads,
+                  const void *k_norm_weight, float eps, const int64_t *positions,
+                  const void *cos_sin_cache, int64_t cos_sin_rows, int32_t rotary_dim,
+                  const int64_t *slot_mapping, void *stream, bool packed) {
     if (w == nullptr)
         return fail(DSPARK_E_ARG, "writer is NULL");
     if (num_layers != w->num_layers || num_kv_heads != w->num_kv_heads)
@@ -70,7 +74,7 @@ extern "C" int dspark_ctx_kv_writer_project_write(
         return fail(DSPARK_E_ARG, "positions and slot_mapping must be 8-byte aligned");
     if (cos_sin_rows <= 0)
         return fail(DSPARK_E_ARG, "cos_sin_cache has no rows");
-    // the kernel addresses states and kv_weight with 32-bit byte offsets
+    // the kernels address states and kv_weight with 32-bit byte offsets
     // (one tile of 256 rows past the end included)
     const int64_t cols = int64_t{num_layers} * 2 * num_kv_heads * DSPARK_HEAD_DIM;
     if ((num_ctx + 256) * hidden * 2 >= (int64_t{1} << 31) || cols * hidden * 2 >= (int64_t{1} << 31))
@@ -91,8 +95,7 @@ extern "C" int dspark_ctx_kv_writer_project_write(
     a.scale0 = w->scale0;
     a.num_ctx = static_cast<uint32_t>(num_ctx);
     a.hidden = hidden;
-    a.cols = static_cast<uint32_t>(num_layers) * 2u * static_cast<uint32_t>(num_kv_heads) *
-             DSPARK_HEAD_DIM;
+    a.cols = static_cast<uint32_t>(cols);
     a.num_layers = w->num_layers;
     a.nkv = w->num_kv_heads;
     a.bs_log2 = w->bs_log2;
@@ -101,7 +104,56 @@ extern "C" int dspark_ctx_kv_writer_project_write(
     memcpy(a.kscale_off, w->kscale_off, sizeof a.kscale_off);
     memcpy(a.vscale_off, w->vscale_off, sizeof a.vscale_off);
     const hipError_t e = dspark::launch_project_write(
-        a, rotary_dim, w->kv_cache_dtype == DSPARK_KV_FP8_E4M3, static_cast<hipStream_t>(stream));
+        a, rotary_dim, w->kv_cache_dtype == DSPARK_KV_FP8_E4M3, packed,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DSPARK_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" int dspark_ctx_kv_writer_project_write(
+    dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, int32_t hidden,
+    const void *kv_weight, int32_t num_layers, int32_t num_kv_heads, const void *k_norm_weight,
+    float eps, const int64_t *positions, const void *cos_sin_cache, int64_t cos_sin_rows,
+    int32_t rotary_dim, const int64_t *slot_mapping, void *stream) {
+    return project_write(w, states, num_ctx, hidden, kv_weight, num_layers, num_kv_heads,
+                         k_norm_weight, eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim,
+                         slot_mapping, stream, false);
+}
+
+extern "C" int dspark_ctx_kv_writer_project_write_packed(
+    dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, int32_t hidden,
+    const void *packed_kv_weight, int32_t num_layers, int32_t num_kv_heads,
+    const void *k_norm_weight, float eps, const int64_t *positions, const void *cos_sin_cache,
+    int64_t cos_sin_rows, int32_t rotary_dim, const int64_t *slot_mapping, void *stream) {
+    return project_write(w, states, num_ctx, hidden, packed_kv_weight, num_layers, num_kv_heads,
+                         k_norm_weight, eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim,
+                         slot_mapping, stream, true);
+}
+
+extern "C" int dspark_kv_weight_pack(const void *kv_weight, int64_t cols, int32_t hidden,
+                                     void *packed, void *stream) {
+    if (cols <= 0 || cols % 32)
+        return fail(DSPARK_E_ARG, "cols %lld is not a positive multiple of 32", (long long)cols);
+    if (hidden <= 0 || hidden % 16)
+        return fail(DSPARK_E_ARG, "hidden %d is not a positive multiple of 16", hidden);
+    if (cols * hidden * 2 >= (int64_t{1} << 31))
+        return fail(DSPARK_E_ARG, "kv_weight exceeds 2 GiB (cols %lld, hidden %d)",
+                    (long long)cols, hidden);
+    if (!kv_weight || !packed)
+        return fail(DSPARK_E_ARG, "a device pointer is NULL");
+    if (!aligned(kv_weight, 16) || !aligned(packed, 16))
+        return fail(DSPARK_E_ARG, "kv_weight and packed must be 16-byte aligned");
+    const uintptr_t src = reinterpret_cast<uintptr_t>(kv_weight);
+    const uintptr_t dst = reinterpret_cast<uintptr_t>(packed);
+    const uintptr_t bytes = static_cast<uintptr_t>(cols * hidden * 2);
+    if (src < dst + bytes && dst < src + bytes)
+        return fail(DSPARK_E_ARG, "packed overlaps kv_weight");
+    const hipError_t e = dspark::launch_pack_kv_weight(
+        static_cast<const uint16_t *>(kv_weight), static_cast<uint16_t *>(packed),
+        static_cast<uint32_t>(cols), hidden, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DSPARK_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return DSPARK_OK;

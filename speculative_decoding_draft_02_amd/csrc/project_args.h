@@ -15,6 +15,7 @@ namespace dspark {
 struct ProjArgs {
     const uint16_t *z;             // bf16 [num_ctx, hidden]: the hidden-norm output
     const uint16_t *W;             // bf16 [cols, hidden]: the projection, [out, in]
+                                   // (or its fragment-major packing)
     const uint16_t *k_norm_weight; // bf16 [L, 128]
     const uint16_t *cos_sin;       // bf16 [rows, R] = [cos | sin]
     const int64_t *positions;      // [num_ctx]
@@ -39,7 +40,16 @@ hipError_t launch_hidden_norm(const uint16_t *x, const uint16_t *w, uint16_t *ou
                               int32_t dim, float eps, hipStream_t stream);
 
 // The projection z @ W^T with the context write of every (layer, kv, head)
-// column block in the epilogue.
-hipError_t launch_project_write(const ProjArgs &args, int rotary_dim, bool fp8, hipStream_t stream);
+// column block in the epilogue; `packed`: W is in the fragment-major layout
+// of launch_pack_kv_weight.
+hipError_t launch_project_write(const ProjArgs &args, int rotary_dim, bool fp8, bool packed,
+                                hipStream_t stream);
+
+// W [cols, hidden] (row-major) -> its fragment-major layout (same size):
+// element (c, k) at fragment (c / 32) * hidden / 16 + k / 16 (512 elements
+// each), position 8 (c % 32 + 32 ((k % 16) / 8)) + k % 8.  cols % 32 == 0,
+// hidden % 16 == 0.
+hipError_t launch_pack_kv_weight(const uint16_t *w, uint16_t *out, uint32_t cols, int32_t hidden,
+                                 hipStream_t stream);
 
 }  // namespace dspark

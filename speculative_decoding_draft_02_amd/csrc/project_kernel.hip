@@ -332,6 +332,26 @@ constexpr int kWaitPrologue = vmcnt_imm((kNSt - 2) * kDLoads + kDLoads / 2);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The tile of this workgroup: 256 tokens (block mb) x 256 columns (block
+// nb).  Workgroup i runs on XCD i % 8, so XCD x takes a contiguous run of
+// the grouped tile order (kGroupM token blocks per group, columns varying
+// between groups).
+struct Tile {
+    uint32_t mb, nb;
+};
+
+__device__ __forceinline__ Tile tile_of(uint32_t num_ctx, uint32_t cols) {
+    const uint32_t mblocks = (num_ctx + kDRows - 1) / kDRows;
+    uint32_t bid = blockIdx.x;
+    const uint32_t full = gridDim.x - gridDim.x % kPNumXcds;
+    if (bid < full) bid = (bid % kPNumXcds) * (full / kPNumXcds) + bid / kPNumXcds;
+    const uint32_t gsz = kGroupM * (cols / 256);
+    const uint32_t gm0 = (bid / gsz) * kGroupM;
+    const uint32_t gm = mblocks - gm0 < kGroupM ? mblocks - gm0 : kGroupM;
+    const uint32_t rem = bid % gsz;
+    return Tile{gm0 + rem % gm, rem / gm};
+}
+
 // 16 bytes per lane from a buffer resource (voff per lane, soff per wave)
 // into LDS at lds + 16 lane (lds wave-uniform)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t res, u32x4 *lds, int voff, int soff) {
@@ -357,20 +377,9 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv % WM;
     const int wn = wv / WM;
-    const uint32_t mblocks = (a.num_ctx + kBM - 1) / kBM;
-    uint32_t bid = blockIdx.x;
-    const uint32_t full = gridDim.x - gridDim.x % kPNumXcds;
-    if (bid < full) bid = (bid % kPNumXcds) * (full / kPNumXcds) + bid / kPNumXcds;
-    // workgroup i runs on XCD i % 8: XCD x takes a contiguous run of the
-    // grouped tile order
-    const uint32_t nblocks = a.cols / (128 * WN);
-    const uint32_t gsz = kGroupM * nblocks;
-    const uint32_t gm0 = (bid / gsz) * kGroupM;
-    const uint32_t gm = mblocks - gm0 < kGroupM ? mblocks - gm0 : kGroupM;
-    const uint32_t rem = bid % gsz;
-    const uint32_t mb = gm0 + rem % gm;
-    const uint32_t nb = rem / gm;
-    const int64_t m0 = static_cast<int64_t>(mb) * kBM;
+    const Tile tile = tile_of(a.num_ctx, a.cols);
+    const uint32_t nb = tile.nb;
+    const int64_t m0 = static_cast<int64_t>(tile.mb) * kBM;
     const int64_t n0 = static_cast<int64_t>(nb) * (128 * WN);
 
     // DMA roles: instruction p of wave wv fills rows 64 p + 16 wv .. + 15 of
@@ -527,11 +536,245 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
         });
 }
 
+// ------------------------------ the projection with a pre-packed weight --
+//
+// The same tile, waves, MFMAs and epilogue as above, with the weight in the
+// fragment-major layout that pack_kv_weight_kernel writes: every 32 x 16
+// weight fragment of the MFMA is 1 KB contiguous, lane l's 16 bytes at
+// 16 l.  A wave then loads its weight fragments straight into registers,
+// 1 KB per instruction in whole cache lines, and the weight never passes
+// through LDS: per stage the CU's LDS moves 48 KB instead of 96 KB, and the
+// L2 serves the weight in 128-byte lines instead of 64-byte halves.  The
+// token rows still go through LDS by DMA, in a ring of four 16 KB stages;
+// the weight goes through a ring of four register stages (32 registers
+// each).  The two waves that share a weight column block both load it.
+constexpr int kPkStage = kDRows * kDK / 8;   // 16-byte chunks of a token stage (16 KB)
+constexpr int kPkRing = 4;                   // stages in flight, in LDS and in registers
+constexpr int kPkSpare = (10 - kPkRing) * kPkStage;   // the rest of 160 KB, for the epilogue
+// Per stage a wave issues kPkBLoads weight loads, then (after the barrier)
+// kPkALoads token loads; with a ring of n stages the token loads of stage
+// j + 1 are followed in issue order by the weight loads of stages j + 1 ..
+// j + n - 1 and the token loads of j + 2 .. j + n - 1 (the steady-state
+// wait).  The prologue waits for stage 0 with one more token stage in
+// flight; the last stages wait as if every weight load after the awaited
+// token loads were gone (they are dead there, and the compiler may drop
+// them).
+constexpr int kPkALoads = 4, kPkBLoads = 8;
+constexpr int kPkWaitStage = vmcnt_imm((kPkRing - 1) * kPkBLoads + (kPkRing - 2) * kPkALoads);
+constexpr int kPkWaitPrologue = vmcnt_imm((kPkRing - 1) * (kPkBLoads + kPkALoads));
+constexpr int kPkWaitTail = vmcnt_imm((kPkRing - 2) * kPkALoads);
+static_assert((kPkRing - 1) * (kPkBLoads + kPkALoads) <= 63, "vmcnt holds at most 63");
+
 template <int R, bool kFp8>
-void launch_pw(const ProjArgs &a, hipStream_t stream) {
-    const uint32_t mblocks = (a.num_ctx + kDRows - 1) / kDRows;
-    hipLaunchKernelGGL((project_write_kernel<R, kFp8>), dim3(mblocks * (a.cols / 256)), dim3(256),
-                       0, stream, a);
+__global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const ProjArgs a) {
+    constexpr int WM = 2, WN = 2, TI = 4, kBM = kDRows;
+    // four token stages, then 96 KB that hold a fifth stage (for a ring of
+    // five) and the epilogue's spare area
+    __shared__ u32x4 sa0[kPkStage], sa1[kPkStage], sa2[kPkStage], sa3[kPkStage], rest[6 * kPkStage];
+    static_assert(kPkRing == 4 || kPkRing == 5, "the ring's arrays");
+    u32x4 *const sa4 = rest;
+    u32x4 *const spare = rest + (kPkRing - 4) * kPkStage;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv % WM;
+    const int wn = wv / WM;
+    const Tile tile = tile_of(a.num_ctx, a.cols);
+    const uint32_t nb = tile.nb;
+    const int64_t m0 = static_cast<int64_t>(tile.mb) * kBM;
+    const int64_t n0 = static_cast<int64_t>(nb) * (128 * WN);
+
+    const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.z), 0, static_cast<int>(a.num_ctx * 2u * a.hidden), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.W), 0, static_cast<int>(a.cols * 2u * a.hidden), 0x00020000);
+    const int row_bytes = 2 * a.hidden;
+    const int nk = a.hidden / kDK;
+    auto clamp = [&](int k) { return k < nk ? k : nk - 1; };
+
+    // token rows into LDS as in the kernel above (rows past num_ctx read as zero)
+    const int drow = 16 * wv + (lane >> 2);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const int zoff = (static_cast<int>(m0) + drow) * row_bytes + dchunk * 16;
+    const int pstep = 64 * row_bytes;
+    auto issue_a = [&](u32x4 *st, int kt) {
+        const int ko = kt * (kDK * 2);
+#pragma unroll
+        for (int p = 0; p < kPkALoads; ++p)
+            dma16(zres, st + (64 * p + 16 * wv) * 4, zoff, p * pstep + ko);
+    };
+
+    // weight fragments into registers: fragment (column block cb, k block
+    // kb) sits at byte (cb * hidden / 16 + kb) * 1024; this wave's column
+    // blocks are (n0 + 128 wn) / 32 + n, and stage kt holds k blocks 2 kt + s
+    const int boff = (static_cast<int>(n0) + 128 * wn) * row_bytes + 16 * lane;
+    const int nstep = 32 * row_bytes;            // one column block of fragments
+    bf16x8 fb[kPkRing][2][4];
+    auto issue_b = [&](int slot, int kt) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                fb[slot][s][n] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wres, boff + 1024 * s,
+                                                                  kt * 2048 + n * nstep, 0));
+    };
+
+    const int hi = lane >> 5;
+    const int cl = lane & 31;
+    const int wrow = 32 * TI * wm;
+    const int arow = (wrow + cl) * 4;
+    const int xs0 = hi ^ ((cl >> 2) & 3);
+    const int xs1 = (2 + hi) ^ ((cl >> 2) & 3);
+
+    int64_t my_pos = 0;
+    if (tid < kBM) {
+        int64_t t = m0 + tid;
+        if (t >= a.num_ctx) t = a.num_ctx - 1;
+        my_pos = a.positions[t];
+    }
+    int64_t my_slot[TI / 2];
+#pragma unroll
+    for (int u = 0; u < TI / 2; ++u) {
+        const int64_t t = m0 + wrow + 64 * u + lane;
+        my_slot[u] = t < a.num_ctx ? a.slots[t] : -1;
+    }
+
+    f32x16 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = f32x16{};
+
+    bf16x8 fa[2][TI];
+    auto read_frags = [&](int buf, const u32x4 *st, int xs) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+            fa[buf][i] = __builtin_bit_cast(bf16x8, st[arow + 128 * i + xs]);
+    };
+    auto mfmas = [&](int slot, int s) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][s][n], fa[s][i],
+                                                                    acc[i][n], 0, 0, 0);
+    };
+    // per group of four MFMAs: one LDS read and two (k step 0: the weight
+    // loads) or one (k step 1: the token loads) memory loads
+    auto interleave0 = [&]() {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+    auto interleave1 = [&]() {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+    // Stage kt (token stage cur, weight slot `slot`): k step 0's MFMAs run
+    // while step 1's token operands are read and the weight of stage kt + 3
+    // is requested; then the token rows of stage kt + 1 are awaited, this
+    // wave's LDS reads drained, and the barrier publishes stage kt + 1 and
+    // retires cur, whose refill with stage kt + 4 goes out during step 1.
+    auto stage = [&](u32x4 *cur, u32x4 *nxt, int slot, int kt, bool last) {
+        read_frags(1, cur, xs1);
+        issue_b((slot + kPkRing - 1) % kPkRing, clamp(kt + kPkRing - 1));
+        mfmas(slot, 0);
+        interleave0();
+        if (last)
+            __builtin_amdgcn_s_waitcnt(kPkWaitTail);
+        else
+            __builtin_amdgcn_s_waitcnt(kPkWaitStage);
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        issue_a(cur, clamp(kt + kPkRing));
+        read_frags(0, nxt, xs0);
+        mfmas(slot, 1);
+        interleave1();
+    };
+
+    u32x4 *const stp[5] = {sa0, sa1, sa2, sa3, sa4};
+    // prologue, in issue order: tokens 0, weight 0, tokens 1, weight 1, ...,
+    // weight n - 2, tokens n - 1
+#pragma unroll
+    for (int j = 0; j < kPkRing - 1; ++j) {
+        issue_a(stp[j], clamp(j));
+        issue_b(j, clamp(j));
+    }
+    issue_a(stp[kPkRing - 1], clamp(kPkRing - 1));
+    __builtin_amdgcn_s_waitcnt(kPkWaitPrologue);
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, sa0, xs0);
+    // whole rounds of the rings while more than one round is left, then the
+    // last ones (at most a round)
+    int kt = 0;
+    for (; kt + kPkRing < nk; kt += kPkRing) {
+#pragma unroll
+        for (int j = 0; j < kPkRing; ++j)
+            stage(stp[j], stp[(j + 1) % kPkRing], j, kt + j, false);
+    }
+#pragma unroll
+    for (int j = 0; j < kPkRing; ++j)
+        if (kt + j < nk) stage(stp[j], stp[(j + 1) % kPkRing], j, kt + j, true);
+    // every load (the clamped reloads too) has landed before the LDS is
+    // reused for the finished tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
+    __syncthreads();
+
+    // the epilogue's LDS: the tile's cos/sin rows at the start of the spare
+    // area, the finished tile's rows over the rest of it, then the token
+    // stages
+    uint8_t *const sp = reinterpret_cast<uint8_t *>(spare);
+    project_epilogue<R, kFp8, WM, WN, TI, kBM>(
+        a, acc, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(spare),
+        [&](int row) {
+            constexpr int kRowBytes = kFp8 ? 128 : 256;
+            constexpr int kCsBytes = kBM * 64 * 2;
+            constexpr int kSpareRows = (kPkSpare * 16 - kCsBytes) / kRowBytes;
+            constexpr int kStageRows = kPkStage * 16 / kRowBytes;
+            static_assert(kSpareRows + kPkRing * kStageRows >= WN * kBM, "the finished tile fits");
+            if (row < kSpareRows) return sp + kCsBytes + row * kRowBytes;
+            const int r = row - kSpareRows;
+            const int q = r / kStageRows;
+            u32x4 *base = q == 0 ? sa0 : q == 1 ? sa1 : q == 2 ? sa2 : q == 3 ? sa3 : sa4;
+            return reinterpret_cast<uint8_t *>(base) + (r % kStageRows) * kRowBytes;
+        });
+}
+
+// The weight's fragment-major layout: element (c, k) of the [cols, hidden]
+// weight goes to fragment (c / 32) * hidden / 16 + k / 16 (1 KB each), lane
+// c % 32 + 32 ((k % 16) / 8), element k % 8 of that lane's 16 bytes.  One
+// thread per 16-byte output chunk (writes contiguous, reads 16 bytes per
+// weight row).
+__global__ __launch_bounds__(256) void pack_kv_weight_kernel(const u32x4 *w, u32x4 *out,
+                                                             uint32_t chunks, int32_t hidden) {
+    const uint32_t q = blockIdx.x * 256u + threadIdx.x;
+    if (q >= chunks) return;
+    const uint32_t frag = q / 64, lane = q % 64;
+    const uint32_t kblocks = static_cast<uint32_t>(hidden) / 16;
+    const uint32_t c = (frag / kblocks) * 32 + lane % 32;
+    const uint32_t k = (frag % kblocks) * 16 + (lane / 32) * 8;
+    out[q] = w[(static_cast<uint64_t>(c) * hidden + k) / 8];
+}
+
+template <int R, bool kFp8>
+void launch_pw(const ProjArgs &a, bool packed, hipStream_t stream) {
+    const dim3 grid((a.num_ctx + kDRows - 1) / kDRows * (a.cols / 256));
+    if (packed)
+        hipLaunchKernelGGL((project_write_packed_kernel<R, kFp8>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((project_write_kernel<R, kFp8>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace
@@ -547,13 +790,23 @@ hipError_t launch_hidden_norm(const uint16_t *x, const uint16_t *w, uint16_t *ou
     return hipGetLastError();
 }
 
-hipError_t launch_project_write(const ProjArgs &a, int rotary_dim, bool fp8, hipStream_t stream) {
+hipError_t launch_project_write(const ProjArgs &a, int rotary_dim, bool fp8, bool packed,
+                                hipStream_t stream) {
     switch (rotary_dim) {
-    case 16: fp8 ? launch_pw<16, true>(a, stream) : launch_pw<16, false>(a, stream); break;
-    case 32: fp8 ? launch_pw<32, true>(a, stream) : launch_pw<32, false>(a, stream); break;
-    case 64: fp8 ? launch_pw<64, true>(a, stream) : launch_pw<64, false>(a, stream); break;
+    case 16: fp8 ? launch_pw<16, true>(a, packed, stream) : launch_pw<16, false>(a, packed, stream); break;
+    case 32: fp8 ? launch_pw<32, true>(a, packed, stream) : launch_pw<32, false>(a, packed, stream); break;
+    case 64: fp8 ? launch_pw<64, true>(a, packed, stream) : launch_pw<64, false>(a, packed, stream); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_kv_weight(const uint16_t *w, uint16_t *out, uint32_t cols, int32_t hidden,
+                                 hipStream_t stream) {
+    const uint32_t chunks = cols * static_cast<uint32_t>(hidden) / 8;
+    hipLaunchKernelGGL(pack_kv_weight_kernel, dim3((chunks + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4 *>(w), reinterpret_cast<u32x4 *>(out), chunks,
+                       hidden);
     return hipGetLastError();
 }
 

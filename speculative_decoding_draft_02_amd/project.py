@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from .writer import DSparkContextKVWriter
+from .writer import DSparkContextKVWriter, PackedKVWeight
 
 
 def hidden_norm(x: torch.Tensor, weight: torch.Tensor, eps: float,
@@ -35,14 +35,33 @@ def hidden_norm(x: torch.Tensor, weight: torch.Tensor, eps: float,
     return out
 
 
+def pack_kv_weight(kv_weight: torch.Tensor) -> PackedKVWeight:
+    """The projection weight (bf16 [cols, hidden], cols % 32 == 0,
+    hidden % 16 == 0) in the fragment-major layout the packed projection
+    kernel loads straight into registers; a permutation, done once per
+    weight."""
+    if kv_weight.dim() != 2 or kv_weight.dtype != torch.bfloat16 or \
+            not kv_weight.is_contiguous() or not kv_weight.is_cuda:
+        raise ValueError("kv_weight must be a contiguous bf16 [cols, hidden] device tensor")
+    cols, hidden = kv_weight.shape
+    out = torch.empty(cols * hidden, dtype=torch.bfloat16, device=kv_weight.device)
+    st = _lib.dspark_kv_weight_pack(kv_weight.data_ptr(), cols, hidden, out.data_ptr(),
+                                    torch.cuda.current_stream(kv_weight.device).cuda_stream)
+    if st != _lib.OK:
+        raise RuntimeError("packing the K/V weight failed: " + _lib.dspark_ctx_kv_last_error())
+    return PackedKVWeight(out, cols, hidden)
+
+
 def precompute_and_store_context_kv(writer: DSparkContextKVWriter, context_states: torch.Tensor,
                                     hidden_norm_weight: torch.Tensor, eps: float,
-                                    kv_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                                    kv_weight: "torch.Tensor | PackedKVWeight",
+                                    k_norm_weight: torch.Tensor,
                                     positions: torch.Tensor, cos_sin_cache: torch.Tensor,
                                     rotary_dim: int, slot_mapping: torch.Tensor,
                                     workspace: torch.Tensor | None = None) -> None:
     """hidden_norm(context_states) into `workspace` (allocated when None),
-    then the projection with every draft layer's context write fused in."""
+    then the projection with every draft layer's context write fused in
+    (kv_weight row-major, or packed by pack_kv_weight)."""
     z = hidden_norm(context_states, hidden_norm_weight, eps, out=workspace)
     writer.project_write(z, kv_weight, k_norm_weight, eps, positions, cos_sin_cache, rotary_dim,
                          slot_mapping)

@@ -564,3 +564,29 @@ def project_exact(num_ctx, hidden, num_layers, num_kv_heads, rotary_dim, block_s
     return ProjectWorkload("project_exact", N, hidden, L, nkv, rotary_dim, block_size, num_blocks,
                            fp8, 1e-6, z, np.zeros(hidden, np.uint16), W, kw, positions, slots,
                            rope_table(rows, rotary_dim), ks, vs, normalized=True)
+
+
+def project_custom(num_ctx, hidden, num_layers, num_kv_heads, rotary_dim, block_size,
+                   num_blocks, fp8, seed, pad_fraction=0.1) -> ProjectWorkload:
+    """Gaussian states (taken as the hidden-norm output) and weight of any
+    shape: z ~ N(0, 1), W ~ N(0, 1 / hidden), slots unique in the cache,
+    positions uniform over a table of num_ctx + 64 rows."""
+    rng = np.random.default_rng(seed)
+    N, L, nkv = num_ctx, num_layers, num_kv_heads
+    C = L * 2 * nkv * HEAD_DIM
+    z = _normal_bf16(rng, (N, hidden), 1.0)
+    W = _normal_bf16(rng, (C, hidden), 1.0 / np.sqrt(hidden))
+    kw = _normal_bf16(rng, (L, HEAD_DIM), 0.1)
+    if fp8:
+        ks = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+        vs = rng.uniform(0.05, 0.5, size=L).astype(np.float32)
+    else:
+        ks = np.ones(L, np.float32)
+        vs = np.ones(L, np.float32)
+    slots = rng.permutation(num_blocks * block_size)[:N].astype(np.int64)
+    slots = _pad(rng, slots, int(round(pad_fraction * N)))
+    rows = N + 64
+    positions = rng.integers(0, rows, size=N).astype(np.int64)
+    return ProjectWorkload("project_custom", N, hidden, L, nkv, rotary_dim, block_size, num_blocks,
+                           fp8, 1e-6, z, np.zeros(hidden, np.uint16), W, kw, positions, slots,
+                           rope_table(rows, rotary_dim), ks, vs, normalized=True)

@@ -77,6 +77,19 @@ class AttnLayer:
     kv_cache_dtype: str = "auto"
 
 
+class PackedKVWeight:
+    """A K/V projection weight in the fragment-major layout of
+    dspark_kv_weight_pack (include/dspark_project.h): `data` is a bf16
+    tensor of cols * hidden elements on the weight's device.  Made by
+    project.pack_kv_weight."""
+
+    def __init__(self, data: torch.Tensor, cols: int, hidden: int):
+        if data.dtype != torch.bfloat16 or data.numel() != cols * hidden or \
+                not data.is_contiguous():
+            raise ValueError("data must be a contiguous bf16 tensor of cols * hidden elements")
+        self.data, self.cols, self.hidden = data, int(cols), int(hidden)
+
+
 class DSparkContextKVWriter:
     """Writes precomputed context K/V into every draft layer's KV cache."""
 
@@ -245,20 +258,27 @@ class DSparkContextKVWriter:
         if st != _lib.OK:
             raise RuntimeError("DSpark context-KV write failed: " + _lib.dspark_ctx_kv_last_error())
 
-    def project_write(self, states: torch.Tensor, kv_weight: torch.Tensor,
+    def project_write(self, states: torch.Tensor, kv_weight: "torch.Tensor | PackedKVWeight",
                       k_norm_weight: torch.Tensor, eps: float, positions: torch.Tensor,
                       cos_sin_cache: torch.Tensor, rotary_dim: int,
                       slot_mapping: torch.Tensor) -> None:
         """The projection all_kv = states @ kv_weight.T with this write fused
         into its epilogue (all_kv is never stored).  states: bf16
         [num_ctx, hidden], the hidden-norm output; kv_weight: bf16
-        [L * 2 * nkv * 128, hidden] ([out, in], rows in all_kv's order);
-        slot_mapping: one int64 [num_ctx] tensor shared by every layer."""
+        [L * 2 * nkv * 128, hidden] ([out, in], rows in all_kv's order), or
+        that weight packed by project.pack_kv_weight (same results, bit for
+        bit); slot_mapping: one int64 [num_ctx] tensor shared by every layer."""
         L, nkv = self._num_layers, self._num_kv_heads
         dev = self._layers[0].kv_cache.device
         if states.dim() != 2:
             raise ValueError("states must be [num_ctx, hidden]")
         num_ctx, hidden = states.shape
+        packed = isinstance(kv_weight, PackedKVWeight)
+        if packed:
+            if (kv_weight.cols, kv_weight.hidden) != (L * 2 * nkv * HEAD_DIM, hidden):
+                raise ValueError(f"the packed weight is for {(kv_weight.cols, kv_weight.hidden)}, "
+                                 f"expected {(L * 2 * nkv * HEAD_DIM, hidden)}")
+            kv_weight = kv_weight.data
         for name, t, dt in (("states", states, torch.bfloat16),
                             ("kv_weight", kv_weight, torch.bfloat16),
                             ("k_norm_weight", k_norm_weight, torch.bfloat16),
@@ -267,7 +287,7 @@ class DSparkContextKVWriter:
                             ("slot_mapping", slot_mapping, torch.int64)):
             if t.dtype != dt or t.device != dev or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
-        if tuple(kv_weight.shape) != (L * 2 * nkv * HEAD_DIM, hidden):
+        if not packed and tuple(kv_weight.shape) != (L * 2 * nkv * HEAD_DIM, hidden):
             raise ValueError(f"kv_weight has shape {tuple(kv_weight.shape)}, "
                              f"expected {(L * 2 * nkv * HEAD_DIM, hidden)}")
         if tuple(k_norm_weight.shape) != (L, HEAD_DIM):
@@ -284,7 +304,9 @@ class DSparkContextKVWriter:
             check_write_preconditions(positions, slot_mapping, cos_sin_cache.shape[0],
                                       c0.shape[0], c0.shape[2])
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = _lib.dspark_ctx_kv_writer_project_write(
+        fn = (_lib.dspark_ctx_kv_writer_project_write_packed if packed
+              else _lib.dspark_ctx_kv_writer_project_write)
+        st = fn(
             self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(), L, nkv,
             k_norm_weight.data_ptr(), float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
             cos_sin_cache.shape[0], int(rotary_dim), slot_mapping.data_ptr(), stream)

@@ -11,7 +11,10 @@ with the context write fused into its epilogue.
 * The full-size pipeline on Gaussian data: every stored value of sampled
   tokens lies in the interval derived from the fp32 accumulation bound
   (oracle/compare.py, write_intervals), at least 99% are bit-exact with the
-  oracle, and every unwritten cache row is untouched."""
+  oracle, and every unwritten cache row is untouched.
+* The packed weight: its layout is the documented permutation (bit-exact),
+  and the projection from it writes the same bytes as the projection from
+  the row-major weight, at small shapes and at the full prefill size."""
 import json
 
 import numpy as np
@@ -20,7 +23,9 @@ import torch
 
 from oracle import compare as C
 from speculative_decoding_draft_02_amd import workloads as W
-from speculative_decoding_draft_02_amd.project import hidden_norm, precompute_and_store_context_kv
+from speculative_decoding_draft_02_amd import _lib
+from speculative_decoding_draft_02_amd.project import (hidden_norm, pack_kv_weight,
+                                                      precompute_and_store_context_kv)
 from speculative_decoding_draft_02_amd.writer import AttnLayer, DSparkContextKVWriter
 from tests._util import bits_to_f32
 
@@ -103,16 +108,18 @@ EXACT_SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("shape", EXACT_SWEEP,
                          ids=lambda s: "N%d-h%d-L%d-kv%d-R%d-bs%d-%s" % (s[0], s[1], s[2], s[3], s[4], s[5],
                                                                       "fp8" if s[7] else "bf16"))
-def test_project_write_exact_grids(oracle_lib, shape):
+def test_project_write_exact_grids(oracle_lib, shape, packed):
     N, hidden, L, nkv, R, bs, nb, fp8, pad = shape
-    print("case project exact", shape, flush=True)
+    print("case project exact", shape, "packed" if packed else "row-major", flush=True)
     wl = W.project_exact(N, hidden, L, nkv, R, bs, nb, fp8, seed=N + hidden, pad_fraction=pad)
     layers = _layers(wl)
     writer = DSparkContextKVWriter(layers)
-    writer.project_write(_bf16(wl.states), _bf16(wl.kv_weight), _bf16(wl.k_norm_weight), wl.eps,
+    weight = pack_kv_weight(_bf16(wl.kv_weight)) if packed else _bf16(wl.kv_weight)
+    writer.project_write(_bf16(wl.states), weight, _bf16(wl.k_norm_weight), wl.eps,
                          torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), R,
                          torch.from_numpy(wl.slot_mapping).to(DEV))
     torch.cuda.synchronize()
@@ -239,13 +246,15 @@ def oracle_lib_e4m3(v):
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def test_project_write_graph_capture(oracle_lib):
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_project_write_graph_capture(oracle_lib, packed):
     """The fused projection/write captured once and replayed: every replay
     writes the oracle's result (the caches are refilled between replays)."""
     wl = W.project_exact(300, 256, 2, 2, 32, 16, 32, True, seed=5)
     layers = _layers(wl)
     writer = DSparkContextKVWriter(layers)
-    args = (_bf16(wl.states), _bf16(wl.kv_weight), _bf16(wl.k_norm_weight), wl.eps,
+    weight = pack_kv_weight(_bf16(wl.kv_weight)) if packed else _bf16(wl.kv_weight)
+    args = (_bf16(wl.states), weight, _bf16(wl.k_norm_weight), wl.eps,
             torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), wl.rotary_dim,
             torch.from_numpy(wl.slot_mapping).to(DEV))
     writer.project_write(*args)
@@ -295,3 +304,78 @@ def test_project_write_debug_checks(oracle_lib):
                                   ww.k_scales, ww.v_scales)
     assert C.compare(got, ref, ww.slot_mapping, False, ww.sentinel).failures == 0
     writer.close()
+
+
+def _packed_reference(w_bits):
+    """The documented fragment-major index of every weight element, applied
+    with numpy: element (c, k) at ((c // 32) * (hidden // 16) + k // 16) * 512
+    + 8 * (c % 32 + 32 * ((k % 16) // 8)) + k % 8."""
+    cols, hidden = w_bits.shape
+    c = np.arange(cols)[:, None]
+    k = np.arange(hidden)[None, :]
+    idx = ((c // 32) * (hidden // 16) + k // 16) * 512 + 8 * (c % 32 + 32 * ((k % 16) // 8)) + k % 8
+    out = np.zeros(cols * hidden, np.uint16)
+    out[idx.reshape(-1)] = w_bits.reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("cols,hidden", [(32, 16), (96, 80), (2560, 6144)])
+def test_pack_kv_weight_layout(cols, hidden):
+    """The packing is a permutation onto the documented index (every input
+    bit pattern moved, none changed), checked against numpy."""
+    rng = np.random.default_rng(cols + hidden)
+    w_bits = rng.integers(0, 1 << 16, size=(cols, hidden), dtype=np.uint16)
+    packed = pack_kv_weight(_bf16(w_bits))
+    torch.cuda.synchronize()
+    assert (packed.cols, packed.hidden) == (cols, hidden)
+    got = packed.data.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _packed_reference(w_bits))
+
+
+def test_pack_kv_weight_errors():
+    """Sizes the layout cannot take and overlapping buffers are refused
+    before any launch, with a reason."""
+    w = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(64 * 64, dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    assert _lib.dspark_kv_weight_pack(w.data_ptr(), 48, 64, out.data_ptr(), s) == _lib.E_ARG
+    assert "multiple of 32" in _lib.dspark_ctx_kv_last_error()
+    assert _lib.dspark_kv_weight_pack(w.data_ptr(), 64, 24, out.data_ptr(), s) == _lib.E_ARG
+    assert "multiple of 16" in _lib.dspark_ctx_kv_last_error()
+    assert _lib.dspark_kv_weight_pack(w.data_ptr(), 64, 64, w.data_ptr() + 1024, s) == _lib.E_ARG
+    assert "overlaps" in _lib.dspark_ctx_kv_last_error()
+    with pytest.raises(ValueError):
+        pack_kv_weight(w.t())
+
+
+def _run_projection(wl, weight, R=None):
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    writer.project_write(_bf16(wl.states), weight, _bf16(wl.k_norm_weight), wl.eps,
+                         torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin),
+                         R or wl.rotary_dim, torch.from_numpy(wl.slot_mapping).to(DEV))
+    torch.cuda.synchronize()
+    got = [_codes(a.kv_cache) for a in layers]
+    writer.close()
+    return got
+
+
+@pytest.mark.parametrize("case", ["small-bf16", "small-fp8", "tail-bf16", "full-bf16", "full-fp8"])
+def test_packed_projection_equals_row_major(case):
+    """The packed kernel accumulates the same products in the same order as
+    the row-major one, so the caches it writes are identical byte for byte:
+    on Gaussian data (no exact grid), with a ragged token tail and a k range
+    that ends inside a ring round, and at the full prefill size."""
+    if case == "small-bf16":
+        wl = W.project_custom(777, 448, 2, 2, 64, 16, 64, False, seed=31, pad_fraction=0.1)
+    elif case == "small-fp8":
+        wl = W.project_custom(513, 960, 3, 1, 32, 8, 256, True, seed=32, pad_fraction=0.2)
+    elif case == "tail-bf16":
+        wl = W.project_custom(33, 64, 1, 2, 16, 4, 16, False, seed=33, pad_fraction=0.0)
+    else:
+        wl = W.project_make(1 if case == "full-bf16" else 2)
+    print("case packed == row-major", case, flush=True)
+    ref = _run_projection(wl, _bf16(wl.kv_weight))
+    got = _run_projection(wl, pack_kv_weight(_bf16(wl.kv_weight)))
+    for l, (g, r) in enumerate(zip(got, ref)):
+        assert np.array_equal(g, r), (case, l, int(np.count_nonzero(g != r)))
