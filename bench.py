@@ -789,7 +789,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": h["kernel_GB_s"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": h["kernel_GB_s"] / HBM_PEAK_GBS,
                            "traffic": traffic_for(head),
-                           "kernel": "ctx_kv_write_kernel<R=64, bf16 cache, 5 layers, uniform token>",
+                           "kernel": "ctx_kv_write_kernel<R=64, bf16 cache, one layer per wave, uniform token>",
                            "kernel_us_avg": h["kernel_us_avg"],
                            "algorithmic_bytes_per_launch": h["bytes_per_call"]}
     else:

@@ -53,19 +53,34 @@ namespace {
 // the bf16 prefill while its stores were nontemporal; with the sc1 stores
 // four waves are 0.8% faster, and they are faster on small and fp8 writes.)
 constexpr int kWavesPerGroup = 4;
-// Writes of at most this many 4-row waves give each layer its own wave
-// (bf16 caches, fp8 caches: the fp8 store's longer arithmetic gains up to
-// larger writes).  Measured under graph replay, L = 5: the split saves 0.7 us
-// of 3.2 on a 300-wave decode write and 6% at 1500 waves (bf16) and 2400
-// (fp8), and loses 8-14% at 2000 (bf16) and 4000 (fp8) waves.
+// Writes of at most this many 4-row waves give each layer its own wave, by
+// row mapping (a wave's rows are heads of one token, or the general mapping)
+// and cache type.  Measured at L = 5 (medians of 5-9 rounds, prefill token
+// subsets, head shards and the long layout as bf16):
+//   * one token per wave, bf16: the split saves 3.9% at 8192 waves (the
+//     4096-token prefill), 7% at 4096, 3.6% at 16384, nothing at 32768 and
+//     loses 1.8% at 65536;
+//   * one token per wave, fp8: it saves 0.7 us of 3.2 on a 300-wave write
+//     and 6% at 2400 waves, and loses 2-6% at 4096 waves and beyond;
+//   * the general mapping (nkv = 2): bf16 gains at 1024 waves (5.85 vs 6.31
+//     us) and is even at 2048; fp8 gains at 1536 (7.86 vs 8.47 us) and loses
+//     12% at 2048 (10.0 vs 8.8 us).
 #ifndef DSPARK_SPLIT_MAX_WAVES_BF16
-#define DSPARK_SPLIT_MAX_WAVES_BF16 1536
+#define DSPARK_SPLIT_MAX_WAVES_BF16 16384
 #endif
 #ifndef DSPARK_SPLIT_MAX_WAVES_FP8
 #define DSPARK_SPLIT_MAX_WAVES_FP8 3072
 #endif
+#ifndef DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16
+#define DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16 1536
+#endif
+#ifndef DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8
+#define DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8 1536
+#endif
 constexpr uint32_t kSplitMaxWavesBf16 = DSPARK_SPLIT_MAX_WAVES_BF16;
 constexpr uint32_t kSplitMaxWavesFp8 = DSPARK_SPLIT_MAX_WAVES_FP8;
+constexpr uint32_t kSplitMaxWavesGeneralBf16 = DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16;
+constexpr uint32_t kSplitMaxWavesGeneralFp8 = DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
@@ -354,8 +369,10 @@ void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
 template <int R, bool kFp8, int kChunk, bool kSinglePass>
 void launch_one(const CtxKvArgs &a, hipStream_t stream) {
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
-    if (!a.layer_slots_on && a.num_layers > 1 &&
-        waves <= (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)) {
+    const uint32_t max_split = a.nkv % kRowsPerWave == 0
+                                   ? (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)
+                                   : (kFp8 ? kSplitMaxWavesGeneralFp8 : kSplitMaxWavesGeneralBf16);
+    if (!a.layer_slots_on && a.num_layers > 1 && waves <= max_split) {
         launch_split<R, kFp8>(a, waves, stream);
         return;
     }

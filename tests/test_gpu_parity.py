@@ -73,6 +73,9 @@ SWEEP = [
     (3200, 9, 2, 64, 8, 512, False, 0.1),   # L > 8 in chunks
     (4200, 12, 3, 32, 4, 1200, True, 0.1),  # L > 8 in chunks, fp8
     (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8
+    # one token per wave beyond 16384 waves: bf16 without the per-layer split
+    (4200, 2, 16, 32, 16, 300, False, 0.1),
+    (8200, 9, 8, 64, 16, 520, False, 0.02),  # ... and in chunks of 8 layers
 ]
 
 
