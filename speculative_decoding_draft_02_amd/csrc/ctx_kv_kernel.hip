@@ -64,7 +64,10 @@ constexpr int kWavesPerGroup = 4;
 //     and 6% at 2400 waves, and loses 2-6% at 4096 waves and beyond;
 //   * the general mapping (nkv = 2): bf16 gains at 1024 waves (5.85 vs 6.31
 //     us) and is even at 2048; fp8 gains at 1536 (7.86 vs 8.47 us) and loses
-//     12% at 2048 (10.0 vs 8.8 us).
+//     12% at 2048 (10.0 vs 8.8 us);
+//   * per-layer slot mappings (nkv = 8): bf16 gains 9% at 1024 waves, 8% at
+//     4096 and 5.8% at 8192; fp8 gains 22% at 1024, 9% at 2048 and 3% at
+//     4096, and loses 4% at 8192.
 #ifndef DSPARK_SPLIT_MAX_WAVES_BF16
 #define DSPARK_SPLIT_MAX_WAVES_BF16 16384
 #endif
@@ -77,10 +80,18 @@ constexpr int kWavesPerGroup = 4;
 #ifndef DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8
 #define DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8 1536
 #endif
+#ifndef DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_BF16
+#define DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_BF16 16384
+#endif
+#ifndef DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8
+#define DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8 4096
+#endif
 constexpr uint32_t kSplitMaxWavesBf16 = DSPARK_SPLIT_MAX_WAVES_BF16;
 constexpr uint32_t kSplitMaxWavesFp8 = DSPARK_SPLIT_MAX_WAVES_FP8;
 constexpr uint32_t kSplitMaxWavesGeneralBf16 = DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16;
 constexpr uint32_t kSplitMaxWavesGeneralFp8 = DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8;
+constexpr uint32_t kSplitMaxWavesLayerSlotsBf16 = DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_BF16;
+constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
@@ -95,14 +106,15 @@ constexpr int kNumXcds = 8;
 // token's slot and position are wave-uniform (scalar loads, scalar exit).
 // kLayerSlots: every layer has its own slot mapping (layers in different KV
 // cache groups); always with the general row mapping.
-// kLayerSplit (small writes, kChunk = 1): each wave writes one layer of its 4
-// rows; wave w takes layer w % L of row group w / L.  A small batch then
-// spreads over L times more waves, each with an L-th of the arithmetic.
+// kLayerSplit (kChunk = 1; writes up to the thresholds above): each wave
+// writes one layer of its 4 rows; wave w takes layer w % L of row group
+// w / L.  The write then spreads over L times more waves, each with an L-th
+// of the loads and arithmetic, so more of them are in flight at different
+// phases.
 template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform, bool kLayerSlots,
           bool kLayerSplit, int kWavesPerBlock>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const CtxKvArgs a) {
-    static_assert(!kLayerSplit || (kChunk == 1 && kSinglePass && !kLayerSlots),
-                  "a split wave holds one layer");
+    static_assert(!kLayerSplit || (kChunk == 1 && kSinglePass), "a split wave holds one layer");
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4;        // quarter: which of the wave's 4 rows
     const int c = lane & 15;        // 16-byte chunk: elements 8c .. 8c+7
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             dk[j] = load_row16(kv_base + (2 * l) * kv_stride);
             dv[j] = load_row16(kv_base + (2 * l + 1) * kv_stride);
             wv[j] = w_base[l * 16];
-            if constexpr (kLayerSlots) lslot[j] = a.layer_slots[l][t];
+            if constexpr (kLayerSlots) lslot[j] = a.layer_slots[l0 + l][t];
         }
     };
     if constexpr (kUniform) {
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                 store = in_range && s >= 0;
                 const int64_t lb_blk = s >> a.bs_log2;
                 const int64_t lb_off = s & ((int64_t{1} << a.bs_log2) - 1);
-                rbase = a.cache_off[l] +
+                rbase = a.cache_off[l0 + l] +
                         ((((lb_blk * nkv + h) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM));
             }
             // the stores go through a buffer resource on a wave-uniform base
@@ -358,7 +370,10 @@ void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
     const uint32_t split = waves * static_cast<uint32_t>(a.num_layers);
     const dim3 grid((split + 3) / 4);
     const dim3 block(256);
-    if (a.nkv % kRowsPerWave == 0)
+    if (a.layer_slots_on)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, false, true, true, 4>),
+                           grid, block, 0, stream, a);
+    else if (a.nkv % kRowsPerWave == 0)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, true, false, true, 4>),
                            grid, block, 0, stream, a);
     else
@@ -369,10 +384,11 @@ void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
 template <int R, bool kFp8, int kChunk, bool kSinglePass>
 void launch_one(const CtxKvArgs &a, hipStream_t stream) {
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
-    const uint32_t max_split = a.nkv % kRowsPerWave == 0
-                                   ? (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)
-                                   : (kFp8 ? kSplitMaxWavesGeneralFp8 : kSplitMaxWavesGeneralBf16);
-    if (!a.layer_slots_on && a.num_layers > 1 && waves <= max_split) {
+    const uint32_t max_split =
+        a.layer_slots_on ? (kFp8 ? kSplitMaxWavesLayerSlotsFp8 : kSplitMaxWavesLayerSlotsBf16)
+        : a.nkv % kRowsPerWave == 0 ? (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)
+                                    : (kFp8 ? kSplitMaxWavesGeneralFp8 : kSplitMaxWavesGeneralBf16);
+    if (a.num_layers > 1 && waves <= max_split) {
         launch_split<R, kFp8>(a, waves, stream);
         return;
     }

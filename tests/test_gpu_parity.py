@@ -267,6 +267,9 @@ LAYER_SLOT_CASES = [
     (129, 3, 2, 16, 4, 80, False),
     (65, 9, 3, 64, 8, 32, True),       # L > 8: chunked pass
     (257, 4, 5, 32, 128, 8, False),
+    # beyond the per-layer split: whole row groups per wave
+    (2100, 9, 8, 32, 16, 140, True),   # more than 4096 waves, fp8, chunked
+    (8200, 2, 8, 64, 16, 520, False),  # more than 16384 waves, bf16
 ]
 
 
