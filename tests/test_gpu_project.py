@@ -379,3 +379,19 @@ def test_packed_projection_equals_row_major(case):
     got = _run_projection(wl, pack_kv_weight(_bf16(wl.kv_weight)))
     for l, (g, r) in enumerate(zip(got, ref)):
         assert np.array_equal(g, r), (case, l, int(np.count_nonzero(g != r)))
+
+
+def test_packed_weight_for_another_shape_is_refused():
+    """A weight packed for another (cols, hidden) is refused before any
+    launch, and the caches stay untouched."""
+    wl = W.project_exact(64, 128, 1, 2, 32, 16, 8, False, seed=9, pad_fraction=0.0)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    other = pack_kv_weight(torch.zeros(2 * 2 * 128, 192, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="packed weight"):
+        writer.project_write(_bf16(wl.states), other, _bf16(wl.k_norm_weight), wl.eps,
+                             torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin), 32,
+                             torch.from_numpy(wl.slot_mapping).to(DEV))
+    torch.cuda.synchronize()
+    assert all(bool((_codes(a.kv_cache) == 0xFFFF).all()) for a in layers)
+    writer.close()
