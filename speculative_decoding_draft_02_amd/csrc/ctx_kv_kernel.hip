@@ -92,6 +92,25 @@ constexpr uint32_t kSplitMaxWavesGeneralBf16 = DSPARK_SPLIT_MAX_WAVES_GENERAL_BF
 constexpr uint32_t kSplitMaxWavesGeneralFp8 = DSPARK_SPLIT_MAX_WAVES_GENERAL_FP8;
 constexpr uint32_t kSplitMaxWavesLayerSlotsBf16 = DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_BF16;
 constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8;
+// Writes above those thresholds give each wave a group of this many layers
+// (1: every layer of the row group in one wave), when L is larger.  Groups of
+// three, measured at L = 5 (groups {0,1,2}, {3,4}) against whole row groups:
+// fp8 prefill 25.0 -> 23.8 us at 8192 waves, -4.2% at 6144, -1.6% at 4096,
+// long fp8 181.8 -> 176.7 us, per-layer slots fp8 -3.4%; bf16 -2.4% at 65536
+// waves and even at 32768; the general mapping 6% slower (bf16, nkv = 2,
+// 2048 waves) and even for fp8.  Groups of two were mixed.
+#ifndef DSPARK_GROUP_LAYERS_BF16
+#define DSPARK_GROUP_LAYERS_BF16 3
+#endif
+#ifndef DSPARK_GROUP_LAYERS_FP8
+#define DSPARK_GROUP_LAYERS_FP8 3
+#endif
+#ifndef DSPARK_GROUP_LAYERS_GENERAL
+#define DSPARK_GROUP_LAYERS_GENERAL 1
+#endif
+constexpr int kGroupLayersBf16 = DSPARK_GROUP_LAYERS_BF16;
+constexpr int kGroupLayersFp8 = DSPARK_GROUP_LAYERS_FP8;
+constexpr int kGroupLayersGeneral = DSPARK_GROUP_LAYERS_GENERAL;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
@@ -106,19 +125,20 @@ constexpr int kNumXcds = 8;
 // token's slot and position are wave-uniform (scalar loads, scalar exit).
 // kLayerSlots: every layer has its own slot mapping (layers in different KV
 // cache groups); always with the general row mapping.
-// kLayerSplit (kChunk = 1; writes up to the thresholds above): each wave
-// writes one layer of its 4 rows; wave w takes layer w % L of row group
-// w / L.  The write then spreads over L times more waves, each with an L-th
-// of the loads and arithmetic, so more of them are in flight at different
-// phases.
+// kLayerSplit (single pass): each wave writes one group of kChunk layers of
+// its 4 rows (the last group shorter); wave w takes layer group w % ng of row
+// group w / ng.  The write then spreads over ng times more waves, each with
+// an ng-th of the loads and arithmetic, so more of them are in flight at
+// different phases.  One layer per wave up to the thresholds below, groups
+// of three beyond.
 template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform, bool kLayerSlots,
           bool kLayerSplit, int kWavesPerBlock>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const CtxKvArgs a) {
-    static_assert(!kLayerSplit || (kChunk == 1 && kSinglePass), "a split wave holds one layer");
+    static_assert(!kLayerSplit || kSinglePass, "a split wave holds one group of layers");
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4;        // quarter: which of the wave's 4 rows
     const int c = lane & 15;        // 16-byte chunk: elements 8c .. 8c+7
-    const int L = kSinglePass ? kChunk : a.num_layers;       // layers this wave writes
+    int L = kSinglePass ? kChunk : a.num_layers;             // layers this wave writes
     const int Lrow = kLayerSplit ? a.num_layers : L;         // layers per all_kv token row
     const int nkv = a.nkv;
 
@@ -132,9 +152,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                     static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     int l0 = 0;                     // first layer this wave writes
     if constexpr (kLayerSplit) {
-        const uint32_t nl = static_cast<uint32_t>(a.num_layers);
-        l0 = static_cast<int>(wave % nl);
-        wave /= nl;
+        // wave w writes layer group w % ng (kChunk layers, the last one
+        // shorter) of row group w / ng
+        const uint32_t ng = (static_cast<uint32_t>(a.num_layers) + kChunk - 1) / kChunk;
+        l0 = static_cast<int>(wave % ng) * kChunk;
+        wave /= ng;
+        L = a.num_layers - l0 < kChunk ? a.num_layers - l0 : kChunk;
     }
     const uint32_t unit0 = wave * kRowsPerWave;             // first row of the wave
     if (unit0 >= a.num_units) return;
@@ -364,32 +387,43 @@ void launch_wpb(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
 }
 
-// One wave per (row group, layer), four waves per workgroup.
-template <int R, bool kFp8>
+// One wave per (row group, group of kGroup layers), four waves per workgroup.
+template <int R, bool kFp8, int kGroup>
 void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
-    const uint32_t split = waves * static_cast<uint32_t>(a.num_layers);
+    const uint32_t ng = (static_cast<uint32_t>(a.num_layers) + kGroup - 1) / kGroup;
+    const uint32_t split = waves * ng;
     const dim3 grid((split + 3) / 4);
     const dim3 block(256);
     if (a.layer_slots_on)
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, false, true, true, 4>),
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, false, true, true, 4>),
                            grid, block, 0, stream, a);
     else if (a.nkv % kRowsPerWave == 0)
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, true, false, true, 4>),
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, true, false, true, 4>),
                            grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, 1, true, false, false, true, 4>),
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, false, false, true, 4>),
                            grid, block, 0, stream, a);
 }
 
 template <int R, bool kFp8, int kChunk, bool kSinglePass>
 void launch_one(const CtxKvArgs &a, hipStream_t stream) {
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
+    const bool general = !a.layer_slots_on && a.nkv % kRowsPerWave != 0;
     const uint32_t max_split =
         a.layer_slots_on ? (kFp8 ? kSplitMaxWavesLayerSlotsFp8 : kSplitMaxWavesLayerSlotsBf16)
-        : a.nkv % kRowsPerWave == 0 ? (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)
-                                    : (kFp8 ? kSplitMaxWavesGeneralFp8 : kSplitMaxWavesGeneralBf16);
+        : !general       ? (kFp8 ? kSplitMaxWavesFp8 : kSplitMaxWavesBf16)
+                         : (kFp8 ? kSplitMaxWavesGeneralFp8 : kSplitMaxWavesGeneralBf16);
     if (a.num_layers > 1 && waves <= max_split) {
-        launch_split<R, kFp8>(a, waves, stream);
+        launch_split<R, kFp8, 1>(a, waves, stream);
+        return;
+    }
+    constexpr int kGroup = kFp8 ? kGroupLayersFp8 : kGroupLayersBf16;
+    if (kGroup > 1 && !general && a.num_layers > kGroup) {
+        launch_split<R, kFp8, kGroup>(a, waves, stream);
+        return;
+    }
+    if (kGroupLayersGeneral > 1 && general && a.num_layers > kGroupLayersGeneral) {
+        launch_split<R, kFp8, kGroupLayersGeneral>(a, waves, stream);
         return;
     }
     launch_wpb<R, kFp8, kChunk, kSinglePass, kWavesPerGroup>(a, waves, stream);

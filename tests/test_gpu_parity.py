@@ -68,14 +68,17 @@ SWEEP = [
     (33, 4, 5, 64, 32, 4, False, 0.0),
     (257, 6, 7, 16, 2, 200, True, 0.25),
     (16, 2, 2, 32, 16, 1, False, 1.0),      # every token is padding
-    # large enough that each wave writes every layer (no per-layer split)
+    # larger writes: the general mapping (every layer of a row group in one
+    # wave, chunked for L > 8) and uniform fp8 rows
     (2100, 3, 3, 16, 16, 200, False, 0.2),
     (3200, 9, 2, 64, 8, 512, False, 0.1),   # L > 8 in chunks
     (4200, 12, 3, 32, 4, 1200, True, 0.1),  # L > 8 in chunks, fp8
-    (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8
-    # one token per wave beyond 16384 waves: bf16 without the per-layer split
+    (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8: groups of 3 layers
+    (3300, 3, 4, 32, 16, 256, True, 0.05),  # uniform rows, fp8, L = 3: one wave per row group
+    # one token per wave beyond 16384 waves: bf16 in one wave per row group
+    # (L = 2) and in groups of 3 layers (L = 9)
     (4200, 2, 16, 32, 16, 300, False, 0.1),
-    (8200, 9, 8, 64, 16, 520, False, 0.02),  # ... and in chunks of 8 layers
+    (8200, 9, 8, 64, 16, 520, False, 0.02),
 ]
 
 
@@ -267,9 +270,10 @@ LAYER_SLOT_CASES = [
     (129, 3, 2, 16, 4, 80, False),
     (65, 9, 3, 64, 8, 32, True),       # L > 8: chunked pass
     (257, 4, 5, 32, 128, 8, False),
-    # beyond the per-layer split: whole row groups per wave
-    (2100, 9, 8, 32, 16, 140, True),   # more than 4096 waves, fp8, chunked
-    (8200, 2, 8, 64, 16, 520, False),  # more than 16384 waves, bf16
+    # beyond the one-layer split: groups of 3 layers (fp8, L = 9) and whole
+    # row groups (bf16, L = 2)
+    (2100, 9, 8, 32, 16, 140, True),   # more than 4096 waves
+    (8200, 2, 8, 64, 16, 520, False),  # more than 16384 waves
 ]
 
 
