@@ -61,18 +61,19 @@ constexpr int kWavesPerGroup = 4;
 //     4096-token prefill), 7% at 4096, 3.6% at 16384, nothing at 32768 and
 //     loses 1.8% at 65536;
 //   * one token per wave, fp8: it saves 0.7 us of 3.2 on a 300-wave write
-//     and 6% at 2400 waves, and loses 2-6% at 4096 waves and beyond;
+//     and beats groups of three layers at 1024 waves (5.22 vs 5.42 us), but
+//     groups of three are faster from 2048 waves (7.81 vs 8.70 us) on;
 //   * the general mapping (nkv = 2): bf16 gains at 1024 waves (5.85 vs 6.31
 //     us) and is even at 2048; fp8 gains at 1536 (7.86 vs 8.47 us) and loses
 //     12% at 2048 (10.0 vs 8.8 us);
 //   * per-layer slot mappings (nkv = 8): bf16 gains 9% at 1024 waves, 8% at
-//     4096 and 5.8% at 8192; fp8 gains 22% at 1024, 9% at 2048 and 3% at
-//     4096, and loses 4% at 8192.
+//     4096 and 5.8% at 8192; fp8 one layer per wave beats groups of three
+//     at 1024 waves (5.41 vs 6.21 us), groups of three win from 2048 on.
 #ifndef DSPARK_SPLIT_MAX_WAVES_BF16
 #define DSPARK_SPLIT_MAX_WAVES_BF16 16384
 #endif
 #ifndef DSPARK_SPLIT_MAX_WAVES_FP8
-#define DSPARK_SPLIT_MAX_WAVES_FP8 3072
+#define DSPARK_SPLIT_MAX_WAVES_FP8 1536
 #endif
 #ifndef DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16
 #define DSPARK_SPLIT_MAX_WAVES_GENERAL_BF16 1536
@@ -84,7 +85,7 @@ constexpr int kWavesPerGroup = 4;
 #define DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_BF16 16384
 #endif
 #ifndef DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8
-#define DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8 4096
+#define DSPARK_SPLIT_MAX_WAVES_LAYER_SLOTS_FP8 1536
 #endif
 constexpr uint32_t kSplitMaxWavesBf16 = DSPARK_SPLIT_MAX_WAVES_BF16;
 constexpr uint32_t kSplitMaxWavesFp8 = DSPARK_SPLIT_MAX_WAVES_FP8;
