@@ -125,7 +125,8 @@ constexpr int kNumXcds = 8;
 // kUniform: nkv % 4 == 0, so a wave's 4 rows are 4 heads of one token and the
 // token's slot and position are wave-uniform (scalar loads, scalar exit).
 // kLayerSlots: every layer has its own slot mapping (layers in different KV
-// cache groups); always with the general row mapping.
+// cache groups); with the uniform-token mapping each layer's slot is
+// wave-uniform, else every quarter reads its own.
 // kLayerSplit (single pass): each wave writes one group of kChunk layers of
 // its 4 rows (the last group shorter); wave w takes layer group w % ng of row
 // group w / ng.  The write then spreads over ng times more waves, each with
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         h = hu + q;
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
                   ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
-        slot = a.slots[t];
+        slot = kLayerSlots ? 0 : a.slots[t];    // per-layer slots: read per layer
         pos = a.positions[t];
         // The row loads do not depend on the slot: they go out together with
         // the slot load, so the slot's latency overlaps theirs (a padding
@@ -200,8 +201,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         load_chunk(0);
         asm volatile("" ::: "memory");
         // padding: nothing written (a negative position never occurs; testing
-        // it keeps both scalar loads ahead of the branch)
-        if (slot < 0 || pos < 0) return;
+        // it keeps both scalar loads ahead of the branch); with per-layer
+        // slots each layer's store tests its own slot
+        if (!kLayerSlots && (slot < 0 || pos < 0)) return;
     } else if constexpr (kLayerSlots) {
         // Each layer's store has its own slot: every in-range quarter reads
         // its rows (a quarter past the end reads the wave's first row) and
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             // element index of this lane's row start (chunk excluded) in layer l
             int64_t rbase = a.cache_off[l0 + l] + row - c * 8;
             bool store = true;
+            int64_t lrow0 = row0;          // uniform path: quarter 0's row in layer l
             if constexpr (kLayerSlots) {
                 const int64_t s = lslot[j];
                 store = in_range && s >= 0;
@@ -293,6 +296,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                 const int64_t lb_off = s & ((int64_t{1} << a.bs_log2) - 1);
                 rbase = a.cache_off[l0 + l] +
                         ((((lb_blk * nkv + h) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM));
+                if constexpr (kUniform) {
+                    // the token's slot in this layer is wave-uniform
+                    if (!store) continue;
+                    lrow0 = (((lb_blk * nkv + hu) << a.bs_log2) + lb_off) * (2 * DSPARK_HEAD_DIM);
+                }
             }
             // the stores go through a buffer resource on a wave-uniform base
             // with the sc1 policy when every lane's offset fits in 31 bits,
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             __amdgpu_buffer_rsrc_t r;
             uint32_t loff;
             if constexpr (kUniform) {
-                r = wave_rsrc(static_cast<char *>(a.cache0) + (a.cache_off[l0 + l] + row0) * kEsz);
+                r = wave_rsrc(static_cast<char *>(a.cache0) + (a.cache_off[l0 + l] + lrow0) * kEsz);
                 loff = lane_elem * kEsz;
             } else if constexpr (!kLayerSlots) {
                 // the general row mapping (quarters of different tokens, nkv
@@ -377,7 +385,10 @@ template <int R, bool kFp8, int kChunk, bool kSinglePass, int kWavesPerBlock>
 void launch_wpb(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const dim3 block(64 * kWavesPerBlock);
-    if (a.layer_slots_on)
+    if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, true, false,
+                                                kWavesPerBlock>), grid, block, 0, stream, a);
+    else if (a.layer_slots_on)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, false, true, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
     else if (a.nkv % kRowsPerWave == 0)
@@ -395,7 +406,10 @@ void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
     const uint32_t split = waves * ng;
     const dim3 grid((split + 3) / 4);
     const dim3 block(256);
-    if (a.layer_slots_on)
+    if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
+        hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, true, true, true, 4>),
+                           grid, block, 0, stream, a);
+    else if (a.layer_slots_on)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, false, true, true, 4>),
                            grid, block, 0, stream, a);
     else if (a.nkv % kRowsPerWave == 0)
