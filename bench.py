@@ -566,7 +566,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the write is "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the write is "
               "independent per token and per kv head, so ranks would shard without any "
               "exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
