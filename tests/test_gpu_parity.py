@@ -92,13 +92,15 @@ def test_sweep_parity(oracle_lib, shape):
 
 
 # the largest supported shapes: DSPARK_MAX_LAYERS layers (one wave per
-# layer, and whole row groups per wave in chunks of 8 layers), many kv heads,
-# a large block
+# layer, groups of three layers per wave, and whole row groups per wave in
+# chunks of 8 layers), many kv heads, a large block
 MAX_CASES = [
     # N, L, nkv, R, bs, blocks, fp8, pad
     (40, 32, 2, 64, 16, 4, False, 0.1),     # per-layer split
     (40, 32, 2, 32, 16, 4, True, 0.1),
-    (1600, 32, 4, 16, 64, 32, False, 0.05),  # 1600 waves: chunked, not split
+    (1600, 32, 4, 16, 64, 32, False, 0.05),  # 1600 waves, bf16: one layer per wave
+    (1600, 32, 4, 16, 64, 32, True, 0.05),   # ... fp8: eleven groups of 3 layers
+    (3200, 32, 2, 32, 64, 64, False, 0.05),  # general mapping, 1600 waves: chunks of 8
     (50, 2, 64, 64, 16, 8, True, 0.1),      # 64 kv heads
     (300, 2, 2, 32, 2048, 2, False, 0.1),   # 2048-token blocks
 ]
