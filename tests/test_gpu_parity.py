@@ -177,7 +177,9 @@ def test_graph_capture_replays_match_eager(oracle_lib):
     is read at replay time."""
     wl = W.make(4)
     wl2 = W.custom(100, 5, 4, 16, 128, 512, True, seed=9, pad_fraction=0.25)
-    for w in (wl, wl2):
+    # 1700 fp8 waves: the launch with groups of three layers per wave
+    wl3 = W.custom(1700, 5, 4, 32, 128, 512, True, seed=10, pad_fraction=0.05)
+    for w in (wl, wl2, wl3):
         print("case graph", w.name, w.fp8, flush=True)
         layers = make_layers(w)
         writer = DSparkContextKVWriter(layers)

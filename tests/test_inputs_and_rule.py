@@ -47,6 +47,14 @@ def test_insert_and_projection_inputs_are_pinned(index):
     assert _digest(W.project_make(index), PROJECT_FIELDS) == PROJECT_DIGESTS[index]
 
 
+def test_gaussian_projection_inputs_are_pinned():
+    wl = W.project_custom(777, 448, 2, 2, 64, 16, 64, False, seed=31, pad_fraction=0.1)
+    assert _digest(wl, PROJECT_FIELDS) == "05e66dac3b647c56"
+    s = wl.slot_mapping[wl.slot_mapping >= 0]
+    assert np.unique(s).size == s.size and s.max() < wl.num_blocks * wl.block_size
+    assert wl.positions.max() < wl.cos_sin.shape[0]
+
+
 def test_generated_slots_are_unique_and_in_range():
     for index in (0, 1, 2, 4):
         wl = W.make(index)
