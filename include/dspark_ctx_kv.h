@@ -16,8 +16,8 @@
  * [..., 128:256] (V) of layer l's separately allocated paged cache
  * [num_blocks, nkv, block_size, 256], as raw bf16 or as OCP fp8 e4m3 of
  * (fp32 value) / (fp32 per-layer scale), saturating at +-448.  A token whose
- * slot is < 0 is padding: nothing is written for it (its rows may still be
- * read, which the kernel does ahead of the slot to hide the slot's latency).
+ * slot is < 0 is padding: nothing is written for it and its position is not
+ * used (its all_kv rows may still be read, ahead of the slot).
  *
  * The writer is built once from the layers' caches and scales (class
  * DSparkContextKVWriter.__init__ and _validate on that page).  Layer l's cache
@@ -64,47 +64,79 @@ enum {
 
 typedef struct dspark_ctx_kv_writer dspark_ctx_kv_writer; /* opaque */
 
-/* Host-only check of a cache layout, the rules of
- * DSparkContextKVWriter._validate as far as raw pointers and sizes carry them
- * (dtype, contiguity and per-layer shape equality are the caller's: the
- * Python binding checks them on the tensors):
- *   num_layers in 1..DSPARK_MAX_LAYERS ("no layers");
- *   kv_cache_dtype is DSPARK_KV_AUTO or DSPARK_KV_FP8_E4M3;
- *   every cache pointer non-NULL and num_blocks, num_kv_heads, block_size > 0
- *     ("KV cache not bound");
- *   head_dim == 128, i.e. rows of 256 elements ("unexpected cache shape");
- *   block_size a power of two;
- *   every k/v scale pointer non-NULL and 4-byte aligned;
- *   every cache's distance from layer 0's cache a multiple of 16 elements,
- *     and layer 0's cache 16-byte aligned (16-byte vector stores);
- *   every scale's distance from layer 0's k scale a multiple of 4 bytes.
- * kv_caches, k_scales, v_scales are host arrays of num_layers device
- * pointers.  Touches no device.  Returns DSPARK_OK or DSPARK_E_LAYOUT. */
-int dspark_ctx_kv_validate(int32_t num_layers,
-                           void *const *kv_caches,
-                           const float *const *k_scales,
-                           const float *const *v_scales,
-                           int64_t num_blocks, int32_t num_kv_heads,
-                           int32_t block_size, int32_t head_dim,
-                           int32_t kv_cache_dtype);
+/* Element types of a tensor, as the caller's framework reports them. */
+enum {
+    DSPARK_DTYPE_OTHER = 0, /* any type the write does not take */
+    DSPARK_DTYPE_BF16 = 1,
+    DSPARK_DTYPE_UINT8 = 2,
+    DSPARK_DTYPE_FP32 = 3
+};
 
-/* Build a writer for num_layers caches, each [num_blocks, num_kv_heads,
- * block_size, 2 * head_dim] of bf16 (DSPARK_KV_AUTO) or uint8
- * (DSPARK_KV_FP8_E4M3), contiguous.  Validates as dspark_ctx_kv_validate,
- * then computes the per-layer cache offsets (elements from kv_caches[0]) and
- * scale offsets (floats from k_scales[0]).  The scale VALUES are read on the
- * device at every write, so they may change between calls or graph replays;
- * the cache and scale ADDRESSES may not (destroy and create again to re-bind).
- * Allocates host memory only.  On success *out receives the writer and the
- * return is DSPARK_OK; otherwise *out is NULL and the return is
- * DSPARK_E_LAYOUT or DSPARK_E_ARG (out == NULL). */
-int dspark_ctx_kv_writer_create(int32_t num_layers,
-                                void *const *kv_caches,
-                                const float *const *k_scales,
-                                const float *const *v_scales,
-                                int64_t num_blocks, int32_t num_kv_heads,
-                                int32_t block_size, int32_t head_dim,
-                                int32_t kv_cache_dtype,
+/* Most dimensions a tensor description carries. */
+#define DSPARK_MAX_DIMS 8
+
+/* What the library needs to know of one tensor to check a layout without a
+ * framework: its address, element type, where it lives, and its shape and
+ * strides (in elements).  A zeroed record (data NULL) means "no tensor". */
+typedef struct dspark_tensor_info {
+    const void *data;                  /* NULL: the attribute is absent or not a tensor */
+    int32_t dtype;                     /* DSPARK_DTYPE_* */
+    const char *dtype_name;            /* the framework's name of the type, quoted in
+                                          reasons (e.g. "torch.int16"); may be NULL */
+    int32_t on_gpu;                    /* 1: GPU device memory; 0: anything else */
+    int32_t device_index;              /* which GPU, when on_gpu */
+    int32_t ndim;                      /* 0 .. DSPARK_MAX_DIMS */
+    int64_t shape[DSPARK_MAX_DIMS];
+    int64_t strides[DSPARK_MAX_DIMS];  /* elements */
+} dspark_tensor_info;
+
+/* One draft attention layer as the writer sees it: the attributes
+ * DSparkContextKVWriter reads from each layer on the vLLM API page
+ * "vllm.models.minimax_m3.common.ops.dspark_context_kv" (kv_cache,
+ * _k_scale, _v_scale, kv_cache_dtype). */
+typedef struct dspark_layer_info {
+    const char *kv_cache_dtype;  /* "auto", "fp8" or "fp8_e4m3"; NULL: the layer has none */
+    dspark_tensor_info kv_cache; /* [num_blocks, num_kv_heads, block_size, 256] */
+    dspark_tensor_info k_scale;  /* fp32 on the GPU, one value read at every write */
+    dspark_tensor_info v_scale;
+} dspark_layer_info;
+
+/* Host-only check of the layers' cache layout: the rules of
+ * DSparkContextKVWriter._validate on the page above, in its order (layers in
+ * order, and for each layer the rules in this order; the first rule that
+ * fails gives the reason, the page's text):
+ *   num_layers >= 1 and layers non-NULL ("no layers");
+ *   num_layers <= DSPARK_MAX_LAYERS (a limit of this library);
+ *   per layer l:
+ *     kv_cache_dtype is "auto", "fp8" or "fp8_e4m3" ("kv_cache_dtype 'x'");
+ *     the cache is a tensor with elements ("KV cache not bound");
+ *     4 dims, the last 256 = 2 * 128 ("unexpected cache shape (...)");
+ *     block_size = shape[2] a power of two;
+ *     contiguous (strides of a row-major tensor; dims of size 1 free);
+ *     uint8 elements for fp8, bf16 for "auto" ("fp8 cache has dtype ..." /
+ *       "cache has dtype ...");
+ *     _k_scale then _v_scale each an fp32 tensor on a GPU;
+ *     the same shape, strides, element type and kv_cache_dtype as layer 0's
+ *       cache ("layers do not share cache shape/stride/dtype");
+ *     on layer 0's GPU ("layers are on different devices");
+ *     a multiple of 16 elements away from layer 0's cache;
+ *   then the library's own limits: layer 0's cache 16-byte aligned, every
+ *   scale 4-byte aligned, num_kv_heads and block_size below 2^31.
+ * Touches no device.  Returns DSPARK_OK or DSPARK_E_LAYOUT (reason in
+ * dspark_ctx_kv_last_error()). */
+int dspark_ctx_kv_validate(int32_t num_layers, const dspark_layer_info *layers);
+
+/* Build a writer for the layers' caches: validates as
+ * dspark_ctx_kv_validate, then computes the per-layer cache offsets
+ * (elements from layer 0's cache) and scale offsets (floats from layer 0's k
+ * scale) of _ensure_tables.  num_blocks, num_kv_heads and block_size are the
+ * caches' shape[0..2].  The scale VALUES are read on the device at every
+ * write, so they may change between calls or graph replays; the cache and
+ * scale ADDRESSES may not (destroy and create again to re-bind).  Allocates
+ * host memory only.  On success *out receives the writer and the return is
+ * DSPARK_OK; otherwise *out is NULL (when out is not) and the return is
+ * DSPARK_E_LAYOUT, or DSPARK_E_ARG for out == NULL. */
+int dspark_ctx_kv_writer_create(int32_t num_layers, const dspark_layer_info *layers,
                                 dspark_ctx_kv_writer **out);
 
 /* Enqueue the fused write on `stream` (a hipStream_t; NULL = the null
@@ -122,10 +154,11 @@ int dspark_ctx_kv_writer_create(int32_t num_layers,
  *   slot_mapping   int64 [num_ctx]; < 0 = padding, else the cache slot
  * num_layers and num_kv_heads must equal the writer's (the assert in
  * DSparkContextKVWriter.__call__).  num_ctx == 0 returns DSPARK_OK without a
- * launch.  Preconditions NOT checked on the device (as on the page): every
- * position of a non-padding token is in [0, cos_sin_rows), every slot is
- * < num_blocks * block_size, and no two non-padding tokens share a slot
- * (with duplicates either token's values may land).  The buffers must not be
+ * launch.  Preconditions NOT checked on the device (as on the page): the
+ * position of every token with a slot >= 0 is in [0, cos_sin_rows) (a
+ * padding token's position is never used as an index, so it may hold any
+ * value), every slot is < num_blocks * block_size, and no two non-padding
+ * tokens share a slot (with duplicates either token's values may land).  The buffers must not be
  * written by other work while the kernel runs.  Returns DSPARK_OK,
  * DSPARK_E_ARG or DSPARK_E_HIP (launch failure). */
 int dspark_ctx_kv_writer_write(dspark_ctx_kv_writer *w,
@@ -147,7 +180,9 @@ int dspark_ctx_kv_writer_write(dspark_ctx_kv_writer *w,
  * slot_mappings[l][t], and a slot < 0 skips that layer only (the token's rows
  * are still read).  Everything else, including the preconditions, is as for
  * dspark_ctx_kv_writer_write; the pointers are taken by value into the
- * launch, so the host array may be reused after the call.  Returns DSPARK_OK,
+ * launch, so the host array may be reused after the call.  A token's
+ * position is used as an index only if its slot is >= 0 in at least one
+ * layer.  Returns DSPARK_OK,
  * DSPARK_E_ARG (also for a NULL or misaligned mapping) or DSPARK_E_HIP. */
 int dspark_ctx_kv_writer_write_layer_slots(dspark_ctx_kv_writer *w,
                                            const void *all_kv, int64_t num_ctx,

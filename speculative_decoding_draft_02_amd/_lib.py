@@ -22,14 +22,33 @@ OK = 0
 E_LAYOUT = -1
 E_ARG = -2
 E_HIP = -4
+DTYPE_OTHER = 0
+DTYPE_BF16 = 1
+DTYPE_UINT8 = 2
+DTYPE_FP32 = 3
+MAX_DIMS = 8
+
+
+class TensorInfo(ctypes.Structure):
+    """struct dspark_tensor_info."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("dtype_name", ctypes.c_char_p), ("on_gpu", ctypes.c_int32),
+                ("device_index", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * MAX_DIMS), ("strides", ctypes.c_int64 * MAX_DIMS)]
+
+
+class LayerInfo(ctypes.Structure):
+    """struct dspark_layer_info."""
+    _fields_ = [("kv_cache_dtype", ctypes.c_char_p), ("kv_cache", TensorInfo),
+                ("k_scale", TensorInfo), ("v_scale", TensorInfo)]
 
 # every entry point the header declares, with its ctypes signature
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 SIGNATURES = {
-    "dspark_ctx_kv_validate": ([_I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32], ctypes.c_int),
-    "dspark_ctx_kv_writer_create": ([_I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P], ctypes.c_int),
+    "dspark_ctx_kv_validate": ([_I32, _P], ctypes.c_int),
+    "dspark_ctx_kv_writer_create": ([_I32, _P, _P], ctypes.c_int),
     "dspark_ctx_kv_writer_write": ([_P, _P, _I64, _I32, _I32, _P, ctypes.c_float, _P, _P, _I64,
                                     _I32, _P, _P], ctypes.c_int),
     "dspark_ctx_kv_writer_write_layer_slots": ([_P, _P, _I64, _I32, _I32, _P, ctypes.c_float, _P, _P,
@@ -76,22 +95,18 @@ def _ptr_array(ptrs):
     return (ctypes.c_void_p * len(ptrs))(*[int(p) for p in ptrs])
 
 
-def dspark_ctx_kv_validate(num_layers, kv_caches, k_scales, v_scales, num_blocks,
-                           num_kv_heads, block_size, head_dim, kv_cache_dtype) -> int:
-    return load().dspark_ctx_kv_validate(
-        num_layers, ctypes.cast(_ptr_array(kv_caches), _P), ctypes.cast(_ptr_array(k_scales), _P),
-        ctypes.cast(_ptr_array(v_scales), _P), num_blocks, num_kv_heads, block_size, head_dim,
-        kv_cache_dtype)
+def dspark_ctx_kv_validate(num_layers, layers) -> int:
+    """layers: a sequence of LayerInfo (or a ctypes array of them)."""
+    arr = (LayerInfo * max(1, len(layers)))(*layers)
+    return load().dspark_ctx_kv_validate(num_layers, ctypes.cast(arr, _P) if len(layers) else None)
 
 
-def dspark_ctx_kv_writer_create(num_layers, kv_caches, k_scales, v_scales, num_blocks,
-                                num_kv_heads, block_size, head_dim, kv_cache_dtype):
+def dspark_ctx_kv_writer_create(num_layers, layers):
     """Returns (status, writer handle as int or None)."""
+    arr = (LayerInfo * max(1, len(layers)))(*layers)
     out = ctypes.c_void_p(0)
-    st = load().dspark_ctx_kv_writer_create(
-        num_layers, ctypes.cast(_ptr_array(kv_caches), _P), ctypes.cast(_ptr_array(k_scales), _P),
-        ctypes.cast(_ptr_array(v_scales), _P), num_blocks, num_kv_heads, block_size, head_dim,
-        kv_cache_dtype, ctypes.byref(out))
+    st = load().dspark_ctx_kv_writer_create(num_layers, ctypes.cast(arr, _P) if len(layers) else None,
+                                            ctypes.byref(out))
     return st, out.value
 
 

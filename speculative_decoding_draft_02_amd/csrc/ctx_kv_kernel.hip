@@ -8,7 +8,9 @@
 // table row [cos | sin] at the token's position), each result rounded to
 // bf16; V passes unchanged.  Both land in layer l's paged cache row
 // [slot / bs, h, slot % bs, :] (K at 0..127, V at 128..255), as bf16 bits or
-// as OCP e4m3 of value / scale.  Padding slots (< 0) read and write nothing.
+// as OCP e4m3 of value / scale.  Nothing is written for a padding slot
+// (< 0), and the position of a token stored in no layer is never used as a
+// table index (its rows may still be read, ahead of its slot).
 //
 // Work decomposition.  The write moves about 8 KB per token per layer group
 // and does about one flop per byte: it is bound by HBM bandwidth, nothing in
@@ -186,6 +188,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             if constexpr (kLayerSlots) lslot[j] = a.layer_slots[l0 + l][t];
         }
     };
+    // per-layer mappings: whether token t has a slot >= 0 in any of the
+    // wave's layers.  Only such a token's cos/sin row is read, so a token
+    // stored in no layer may carry any position.
+    auto stored_in_any_layer = [&]() {
+        bool any = false;
+        if constexpr (kSinglePass) {
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) any |= (j < L) & (lslot[j] >= 0);
+        } else {
+            for (int l = 0; l < L; ++l) any |= a.layer_slots[l0 + l][t] >= 0;
+        }
+        return any;
+    };
     if constexpr (kUniform) {
         t = unit0 / static_cast<uint32_t>(nkv);
         hu = static_cast<int>(unit0 - t * static_cast<uint32_t>(nkv));
@@ -202,8 +217,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         asm volatile("" ::: "memory");
         // padding: nothing written (a negative position never occurs; testing
         // it keeps both scalar loads ahead of the branch); with per-layer
-        // slots each layer's store tests its own slot
-        if (!kLayerSlots && (slot < 0 || pos < 0)) return;
+        // slots each layer's store tests its own slot, and a token stored in
+        // no layer of the wave ends here, before its cos/sin row is read
+        if constexpr (kLayerSlots) {
+            if (!stored_in_any_layer()) return;
+        } else if (slot < 0 || pos < 0) {
+            return;
+        }
     } else if constexpr (kLayerSlots) {
         // Each layer's store has its own slot: every in-range quarter reads
         // its rows (a quarter past the end reads the wave's first row) and
@@ -218,6 +238,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                   ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         load_chunk(0);
         asm volatile("" ::: "memory");   // keep the loads ahead of the predicated stores
+        // a quarter whose token is stored in no layer (or past the end) reads
+        // cos/sin row 0 instead of its position's row; its stores are off
+        const bool stores = in_range && stored_in_any_layer();
+        if (__ballot(stores) == 0) return;
+        if (!stores) pos = 0;
     } else {
         const uint32_t unit = unit0 + q;                    // (token, kv head) row
         in_range = unit < a.num_units;

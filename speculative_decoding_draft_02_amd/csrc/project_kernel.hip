@@ -420,11 +420,17 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
     const int xs0 = hi ^ ((cl >> 2) & 3);
     const int xs1 = (2 + hi) ^ ((cl >> 2) & 3);
 
+    // tile row tid's position, for the epilogue's cos/sin staging; a row that
+    // stores nothing (a padding slot, or past num_ctx) stages table row 0, so
+    // a padding token's position is never used as an index
     int64_t my_pos = 0;
     if (tid < kBM) {
         int64_t t = m0 + tid;
-        if (t >= a.num_ctx) t = a.num_ctx - 1;
-        my_pos = a.positions[t];
+        const bool inside = t < a.num_ctx;
+        if (!inside) t = a.num_ctx - 1;
+        const int64_t pos = a.positions[t];
+        const int64_t slot = a.slots[t];
+        my_pos = inside && slot >= 0 ? pos : 0;
     }
     int64_t my_slot[TI / 2];
 #pragma unroll
@@ -627,11 +633,17 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
     const int xs0 = hi ^ ((cl >> 2) & 3);
     const int xs1 = (2 + hi) ^ ((cl >> 2) & 3);
 
+    // tile row tid's position, for the epilogue's cos/sin staging; a row that
+    // stores nothing (a padding slot, or past num_ctx) stages table row 0, so
+    // a padding token's position is never used as an index
     int64_t my_pos = 0;
     if (tid < kBM) {
         int64_t t = m0 + tid;
-        if (t >= a.num_ctx) t = a.num_ctx - 1;
-        my_pos = a.positions[t];
+        const bool inside = t < a.num_ctx;
+        if (!inside) t = a.num_ctx - 1;
+        const int64_t pos = a.positions[t];
+        const int64_t slot = a.slots[t];
+        my_pos = inside && slot >= 0 ? pos : 0;
     }
     int64_t my_slot[TI / 2];
 #pragma unroll

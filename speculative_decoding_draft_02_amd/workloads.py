@@ -251,6 +251,22 @@ def per_layer_slots(wl: Workload, seed: int, pad_fraction: float = 0.05) -> Work
     return dataclasses.replace(wl, slot_mapping=maps)
 
 
+def padding_positions_off_table(wl):
+    """The same inputs with the position of every token that is stored in no
+    layer moved off the cos/sin table: -1, rows, -1, rows, ... (rows =
+    cos_sin.shape[0]).  Such a position is never used as an index, so the
+    result of the write must not change.  Takes a Workload or a
+    ProjectWorkload (anything with positions, slot_mapping and cos_sin)."""
+    import dataclasses
+    stored = wl.slot_mapping >= 0
+    if stored.ndim == 2:
+        stored = stored.any(axis=0)
+    pos = wl.positions.copy()
+    idle = np.flatnonzero(~stored)
+    pos[idle] = np.where(np.arange(idle.size) % 2 == 0, -1, wl.cos_sin.shape[0])
+    return dataclasses.replace(wl, positions=pos)
+
+
 def head_shard(wl: Workload, tp: int, rank: int) -> Workload:
     """One rank's share under head (tensor) parallelism: kv heads
     [rank * nkv / tp, (rank + 1) * nkv / tp) of every token and layer, written

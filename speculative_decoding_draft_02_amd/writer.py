@@ -1,12 +1,13 @@
 """PyTorch-facing writer for the DSpark fused context-KV write.
 
-Mirrors class DSparkContextKVWriter and rotary_dims_supported on the vLLM API
-page "vllm.models.minimax_m3.common.ops.dspark_context_kv": built from the
-draft's attention layers (objects carrying ``kv_cache``, ``_k_scale``,
-``_v_scale`` and ``kv_cache_dtype``), validated with the same reasons, with
-the per-layer offset tables keyed by the layers' data pointers and rebuilt
-(outside graph capture only) when a cache is re-bound.  Every step of the
-write runs in the HIP library; this module only checks tensors and passes
+Offers what class DSparkContextKVWriter and rotary_dims_supported offer on
+the vLLM API page "vllm.models.minimax_m3.common.ops.dspark_context_kv": a
+writer built from the draft's attention layers (objects carrying
+``kv_cache``, ``_k_scale``, ``_v_scale`` and ``kv_cache_dtype``), refused with
+the page's reasons when their caches do not fit, and rebuilt (outside graph
+capture only) when a cache or scale is re-bound.  The layout rules and every
+step of the write live in the HIP library: this module describes the
+tensors to it (address, element type, device, shape, strides) and passes
 pointers.  PyTorch supplies device memory and the current stream.
 """
 from __future__ import annotations
@@ -18,7 +19,6 @@ import torch
 from . import _lib
 
 HEAD_DIM = _lib.HEAD_DIM
-SUPPORTED_KV_DTYPES = ("auto", "fp8", "fp8_e4m3")
 
 
 def rotary_dims_supported(rotary_dim: int, head_dim: int) -> bool:
@@ -45,22 +45,26 @@ def _split_slot_mapping(slot_mapping, num_layers):
 
 def check_write_preconditions(positions: torch.Tensor, slot_mapping, cos_sin_rows: int,
                               num_blocks: int, block_size: int) -> None:
-    """The write's preconditions that the kernel does not check (as on the
-    vLLM API page "vllm.models.minimax_m3.common.ops.dspark_context_kv"):
-    every non-padding token's position indexes the cos/sin table, every
-    slot is inside the cache, and no two non-padding tokens of a layer share
-    a slot.  Raises ValueError naming the first violation.  Costs a host
-    sync: meant for debugging (DSparkContextKVWriter(debug_checks=True))."""
+    """The write's preconditions that the kernels do not check (as on the
+    vLLM API page "vllm.models.minimax_m3.common.ops.dspark_context_kv"),
+    exactly as far as the kernels rely on them: the position of every token
+    that is stored in at least one layer indexes the cos/sin table (the
+    positions of tokens stored in no layer are never read), every slot is
+    inside the cache, and no two tokens share a slot within one layer.
+    Raises ValueError naming the first violation.  Costs a host sync: meant
+    for debugging (DSparkContextKVWriter(debug_checks=True))."""
     maps = [slot_mapping] if isinstance(slot_mapping, torch.Tensor) and slot_mapping.dim() == 1 \
         else list(slot_mapping)
+    stored = torch.zeros_like(positions, dtype=torch.bool)
+    for slots in maps:
+        stored |= slots >= 0
+    pos = positions[stored]
+    if pos.numel() and (bool((pos < 0).any()) or bool((pos >= cos_sin_rows).any())):
+        raise ValueError(f"a stored token's position is outside the cos/sin table of "
+                         f"{cos_sin_rows} rows")
     capacity = int(num_blocks) * int(block_size)
     for l, slots in enumerate(maps):
-        valid = slots >= 0
-        pos = positions[valid]
-        if pos.numel() and (bool((pos < 0).any()) or bool((pos >= cos_sin_rows).any())):
-            raise ValueError(f"a position is outside the cos/sin table of {cos_sin_rows} rows "
-                             f"(slot mapping {l})")
-        s = slots[valid]
+        s = slots[slots >= 0]
         if s.numel() and bool((s >= capacity).any()):
             raise ValueError(f"a slot is >= num_blocks * block_size = {capacity} "
                              f"(slot mapping {l})")
@@ -75,6 +79,52 @@ class AttnLayer:
     _k_scale: torch.Tensor
     _v_scale: torch.Tensor
     kv_cache_dtype: str = "auto"
+
+
+_ELEMENT_TYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.uint8: _lib.DTYPE_UINT8,
+                  torch.float32: _lib.DTYPE_FP32}
+
+
+def tensor_info(t) -> _lib.TensorInfo:
+    """The facts of one layer attribute that the library's layout rules use
+    (a zeroed record when the attribute is not a tensor)."""
+    info = _lib.TensorInfo()
+    if not isinstance(t, torch.Tensor):
+        return info
+    info.data = t.data_ptr() or None
+    info.dtype = _ELEMENT_TYPES.get(t.dtype, _lib.DTYPE_OTHER)
+    info.dtype_name = str(t.dtype).encode()
+    info.on_gpu = int(t.is_cuda)
+    info.device_index = t.device.index if t.is_cuda else -1
+    dims = min(t.dim(), _lib.MAX_DIMS)
+    info.ndim = dims
+    info.shape[:dims] = list(t.shape[:dims])
+    info.strides[:dims] = list(t.stride()[:dims])
+    return info
+
+
+def layer_info(layer) -> _lib.LayerInfo:
+    """One attention layer described for dspark_ctx_kv_validate / create."""
+    info = _lib.LayerInfo()
+    name = getattr(layer, "kv_cache_dtype", None)
+    info.kv_cache_dtype = None if name is None else str(name).encode()
+    info.kv_cache = tensor_info(getattr(layer, "kv_cache", None))
+    info.k_scale = tensor_info(getattr(layer, "_k_scale", None))
+    info.v_scale = tensor_info(getattr(layer, "_v_scale", None))
+    return info
+
+
+def layout_error(attn_layers) -> "str | None":
+    """Why the library would refuse these layers' caches (the first broken
+    rule, in the page's words), or None if it accepts them."""
+    infos = [layer_info(a) for a in attn_layers]
+    if _lib.dspark_ctx_kv_validate(len(infos), infos) == _lib.OK:
+        return None
+    return _lib.dspark_ctx_kv_last_error()
+
+
+def _refuse(reason: str) -> ValueError:
+    return ValueError(f"unsupported DSpark context-KV layout: {reason}")
 
 
 class PackedKVWeight:
@@ -97,164 +147,110 @@ class DSparkContextKVWriter:
         """debug_checks: check the preconditions the kernel trusts (positions
         in the table, slots in the cache, no shared slots) on every call,
         at the cost of a host sync per call."""
+        self._layers = list(attn_layers)
+        reason = layout_error(self._layers)
+        if reason is not None:
+            raise _refuse(reason)
+        first = self._layers[0].kv_cache
+        self._num_layers = len(self._layers)
+        self._num_kv_heads = first.shape[1]
         self._debug_checks = bool(debug_checks)
-        layers = list(attn_layers)
-        error = self._validate(layers)
-        if error is not None:
-            raise ValueError(f"unsupported DSpark context-KV layout: {error}")
-        self._layers = layers
-        cache = layers[0].kv_cache
-        self._num_layers = len(layers)
-        self._num_kv_heads = cache.shape[1]
-        self._kv_cache_dtype = "fp8" if cache.dtype == torch.uint8 else "auto"
-        self._table_key = None
-        self._handle = None
-
-    @staticmethod
-    def _validate(layers) -> str | None:
-        if not layers:
-            return "no layers"
-        ref = None
-        for a in layers:
-            kv_dtype = getattr(a, "kv_cache_dtype", None)
-            if kv_dtype not in SUPPORTED_KV_DTYPES:
-                return f"kv_cache_dtype {kv_dtype!r}"
-            cache = getattr(a, "kv_cache", None)
-            if not isinstance(cache, torch.Tensor) or cache.numel() == 0:
-                return "KV cache not bound"
-            if cache.dim() != 4 or cache.shape[3] != 2 * HEAD_DIM:
-                return f"unexpected cache shape {tuple(cache.shape)}"
-            block_size = cache.shape[2]
-            if block_size & (block_size - 1):
-                return f"block size {block_size} is not a power of two"
-            if not cache.is_contiguous():
-                return "cache is not contiguous"
-            if kv_dtype in ("fp8", "fp8_e4m3"):
-                if cache.dtype != torch.uint8:
-                    return f"fp8 cache has dtype {cache.dtype}"
-            elif cache.dtype != torch.bfloat16:
-                return f"cache has dtype {cache.dtype}"
-            for name in ("_k_scale", "_v_scale"):
-                scale = getattr(a, name, None)
-                if (not isinstance(scale, torch.Tensor) or scale.dtype != torch.float32
-                        or not scale.is_cuda):
-                    return f"{name} is not a CUDA fp32 tensor"
-            key = (cache.shape, cache.stride(), cache.dtype, kv_dtype)
-            if ref is None:
-                ref = key
-            elif key != ref:
-                return "layers do not share cache shape/stride/dtype"
-            if cache.device != layers[0].kv_cache.device:
-                return "layers are on different devices"
-            delta = cache.data_ptr() - layers[0].kv_cache.data_ptr()
-            if delta % (16 * cache.element_size()):
-                return "layer caches are not 16-element aligned to each other"
-        # what the raw pointers carry (alignment, limits) is checked by the library
-        c0 = layers[0].kv_cache
-        st = _lib.dspark_ctx_kv_validate(
-            len(layers), [a.kv_cache.data_ptr() for a in layers],
-            [a._k_scale.data_ptr() for a in layers], [a._v_scale.data_ptr() for a in layers],
-            c0.shape[0], c0.shape[1], c0.shape[2], c0.shape[3] // 2,
-            _lib.KV_FP8_E4M3 if c0.dtype == torch.uint8 else _lib.KV_AUTO)
-        if st != _lib.OK:
-            return _lib.dspark_ctx_kv_last_error()
-        return None
+        self._handle = None       # the library's writer
+        self._bound_to = None     # the cache and scale addresses it was built for
 
     @staticmethod
     def supported(attn_layers) -> bool:
-        """True when the HIP library is built, the layers' device is a gfx950
-        GPU (its fp8 store is OCP E4M3) and the layout validates."""
+        """True when the HIP library is built, the layers live on a gfx950
+        GPU (its fp8 conversion is OCP E4M3) and the library accepts their
+        layout."""
         try:
             _lib.load()
         except _lib.LibraryMissing:
             return False
         layers = list(attn_layers)
-        if not layers or not torch.cuda.is_available():
-            return False
-        cache = getattr(layers[0], "kv_cache", None)
+        cache = getattr(layers[0], "kv_cache", None) if layers else None
         if not isinstance(cache, torch.Tensor) or not cache.is_cuda:
             return False
-        arch = torch.cuda.get_device_properties(cache.device).gcnArchName
-        if not arch.startswith("gfx950"):
+        if not torch.cuda.get_device_properties(cache.device).gcnArchName.startswith("gfx950"):
             return False
-        return DSparkContextKVWriter._validate(layers) is None
+        return layout_error(layers) is None
 
-    def _ensure_tables(self) -> None:
-        layers = self._layers
-        key = tuple((a.kv_cache.data_ptr(), a._k_scale.data_ptr(), a._v_scale.data_ptr())
-                    for a in layers)
-        if key == self._table_key:
+    def _addresses(self) -> tuple:
+        return tuple(t.data_ptr() for a in self._layers
+                     for t in (a.kv_cache, a._k_scale, a._v_scale))
+
+    def _bind(self) -> None:
+        """Build the library's writer on first use, and again whenever a
+        layer's cache or scale tensor has been replaced since (never while
+        the stream is being captured: a graph must keep its addresses)."""
+        addresses = self._addresses()
+        if addresses == self._bound_to:
             return
         if torch.cuda.is_current_stream_capturing():
             raise RuntimeError("DSpark context-KV caches were re-bound during graph capture; "
                                "call the writer once outside capture first")
-        error = self._validate(layers)
-        if error is not None:
-            raise ValueError(f"unsupported DSpark context-KV layout: {error}")
-        self.close()
-        c0 = layers[0].kv_cache
-        st, handle = _lib.dspark_ctx_kv_writer_create(
-            len(layers), [a.kv_cache.data_ptr() for a in layers],
-            [a._k_scale.data_ptr() for a in layers], [a._v_scale.data_ptr() for a in layers],
-            c0.shape[0], c0.shape[1], c0.shape[2], c0.shape[3] // 2,
-            _lib.KV_FP8_E4M3 if self._kv_cache_dtype == "fp8" else _lib.KV_AUTO)
+        infos = [layer_info(a) for a in self._layers]
+        st, handle = _lib.dspark_ctx_kv_writer_create(len(infos), infos)
         if st != _lib.OK:
-            raise ValueError("unsupported DSpark context-KV layout: "
-                             + _lib.dspark_ctx_kv_last_error())
-        self._handle = handle
-        self._table_key = key
+            raise _refuse(_lib.dspark_ctx_kv_last_error())
+        self.close()
+        self._handle, self._bound_to = handle, addresses
 
-    def __call__(self, all_kv: torch.Tensor, k_norm_weight: torch.Tensor, eps: float,
-                 positions: torch.Tensor, cos_sin_cache: torch.Tensor, rotary_dim: int,
-                 slot_mapping) -> None:
-        """slot_mapping: one int64 [num_ctx] tensor shared by every layer, or
-        a list of L such tensors (one per layer, as the model passes when its
-        layers span several KV-cache groups), or an int64 [L, num_ctx]
-        tensor.  A list whose entries are all the same tensor is the shared
-        case (the rule of _shared_slot_mapping)."""
-        num_ctx, L, two, nkv, hd = all_kv.shape
-        assert self._num_layers == L and self._num_kv_heads == nkv
-        assert two == 2 and hd == HEAD_DIM
-        if num_ctx == 0:
-            return
+    def _check_inputs(self, num_ctx: int, tensors, slot_tensors) -> None:
+        """Element type, device and contiguity of every input (the library
+        takes raw pointers and cannot see them)."""
         dev = self._layers[0].kv_cache.device
-        shared, per_layer = _split_slot_mapping(slot_mapping, L)
-        for name, t, dt in (("all_kv", all_kv, torch.bfloat16),
-                            ("k_norm_weight", k_norm_weight, torch.bfloat16),
-                            ("positions", positions, torch.int64),
-                            ("cos_sin_cache", cos_sin_cache, torch.bfloat16)):
+        for name, t, dt in tensors:
             if t.dtype != dt or t.device != dev or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
-        for t in ([shared] if shared is not None else per_layer):
+        for t in slot_tensors:
             if t.dtype != torch.int64 or t.device != dev or not t.is_contiguous() \
                     or t.shape != (num_ctx,):
                 raise ValueError(f"slot mappings must be contiguous int64 ({num_ctx},) "
                                  f"tensors on {dev}")
-        if tuple(k_norm_weight.shape) != (L, HEAD_DIM):
+
+    def __call__(self, all_kv: torch.Tensor, k_norm_weight: torch.Tensor, eps: float,
+                 positions: torch.Tensor, cos_sin_cache: torch.Tensor, rotary_dim: int,
+                 slot_mapping) -> None:
+        """all_kv: bf16 [num_ctx, L, 2, nkv, 128] (axis 2: K, V).
+        slot_mapping: one int64 [num_ctx] tensor shared by every layer, or
+        a list of L such tensors (one per layer, as the model passes when its
+        layers span several KV-cache groups), or an int64 [L, num_ctx]
+        tensor.  A list whose entries are all the same tensor is the shared
+        case (the rule of _shared_slot_mapping).  A layer count or kv head
+        count other than the writer's is refused by the library."""
+        if all_kv.dim() != 5 or all_kv.shape[2] != 2 or all_kv.shape[4] != HEAD_DIM:
+            raise ValueError(f"all_kv must be [num_ctx, L, 2, nkv, {HEAD_DIM}], "
+                             f"got {tuple(all_kv.shape)}")
+        num_ctx, num_layers, _, num_kv_heads, _ = all_kv.shape
+        shared, per_layer = _split_slot_mapping(slot_mapping, num_layers)
+        self._check_inputs(num_ctx, (("all_kv", all_kv, torch.bfloat16),
+                                     ("k_norm_weight", k_norm_weight, torch.bfloat16),
+                                     ("positions", positions, torch.int64),
+                                     ("cos_sin_cache", cos_sin_cache, torch.bfloat16)),
+                           [shared] if shared is not None else per_layer)
+        if tuple(k_norm_weight.shape) != (num_layers, HEAD_DIM):
             raise ValueError(f"k_norm_weight has shape {tuple(k_norm_weight.shape)}, "
-                             f"expected {(L, HEAD_DIM)}")
+                             f"expected {(num_layers, HEAD_DIM)}")
         if positions.shape != (num_ctx,):
             raise ValueError("positions must have shape (num_ctx,)")
         if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != rotary_dim:
             raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}, "
                              f"expected (rows, {rotary_dim})")
-        self._ensure_tables()
-        if self._debug_checks:
+        self._bind()
+        if self._debug_checks and num_ctx:
             c0 = self._layers[0].kv_cache
             check_write_preconditions(positions, shared if shared is not None else per_layer,
                                       cos_sin_cache.shape[0], c0.shape[0], c0.shape[2])
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = torch.cuda.current_stream(all_kv.device).cuda_stream
+        common = (self._handle, all_kv.data_ptr(), num_ctx, num_layers, num_kv_heads,
+                  k_norm_weight.data_ptr(), float(eps), positions.data_ptr(),
+                  cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(rotary_dim))
         if shared is not None:
-            st = _lib.dspark_ctx_kv_writer_write(
-                self._handle, all_kv.data_ptr(), num_ctx, L, nkv, k_norm_weight.data_ptr(),
-                float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
-                cos_sin_cache.shape[0], int(rotary_dim), shared.data_ptr(), stream)
+            st = _lib.dspark_ctx_kv_writer_write(*common, shared.data_ptr(), stream)
         else:
             st = _lib.dspark_ctx_kv_writer_write_layer_slots(
-                self._handle, all_kv.data_ptr(), num_ctx, L, nkv, k_norm_weight.data_ptr(),
-                float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
-                cos_sin_cache.shape[0], int(rotary_dim), [t.data_ptr() for t in per_layer],
-                stream)
+                *common, [t.data_ptr() for t in per_layer], stream)
         if st != _lib.OK:
             raise RuntimeError("DSpark context-KV write failed: " + _lib.dspark_ctx_kv_last_error())
 
@@ -279,14 +275,12 @@ class DSparkContextKVWriter:
                 raise ValueError(f"the packed weight is for {(kv_weight.cols, kv_weight.hidden)}, "
                                  f"expected {(L * 2 * nkv * HEAD_DIM, hidden)}")
             kv_weight = kv_weight.data
-        for name, t, dt in (("states", states, torch.bfloat16),
-                            ("kv_weight", kv_weight, torch.bfloat16),
-                            ("k_norm_weight", k_norm_weight, torch.bfloat16),
-                            ("positions", positions, torch.int64),
-                            ("cos_sin_cache", cos_sin_cache, torch.bfloat16),
-                            ("slot_mapping", slot_mapping, torch.int64)):
-            if t.dtype != dt or t.device != dev or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+        self._check_inputs(num_ctx, (("states", states, torch.bfloat16),
+                                     ("kv_weight", kv_weight, torch.bfloat16),
+                                     ("k_norm_weight", k_norm_weight, torch.bfloat16),
+                                     ("positions", positions, torch.int64),
+                                     ("cos_sin_cache", cos_sin_cache, torch.bfloat16),
+                                     ("slot_mapping", slot_mapping, torch.int64)), ())
         if not packed and tuple(kv_weight.shape) != (L * 2 * nkv * HEAD_DIM, hidden):
             raise ValueError(f"kv_weight has shape {tuple(kv_weight.shape)}, "
                              f"expected {(L * 2 * nkv * HEAD_DIM, hidden)}")
@@ -298,7 +292,7 @@ class DSparkContextKVWriter:
             raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}")
         if num_ctx == 0:
             return
-        self._ensure_tables()
+        self._bind()
         if self._debug_checks:
             c0 = self._layers[0].kv_cache
             check_write_preconditions(positions, slot_mapping, cos_sin_cache.shape[0],
@@ -318,7 +312,7 @@ class DSparkContextKVWriter:
         if self._handle is not None:
             _lib.dspark_ctx_kv_writer_destroy(self._handle)
             self._handle = None
-            self._table_key = None
+            self._bound_to = None
 
     def __del__(self):
         try:

@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI: the library loads, exports every entry point
-the header declares, and its host logic (layout validation with the reasons
+the header declares, and its host logic (the layout rules with the reasons
 of DSparkContextKVWriter._validate, argument checks of write, the supported
 rotary dims) behaves as documented.  No call here reaches a GPU: create is
 host-only and every write below is refused or is a no-op before any launch."""
@@ -69,67 +69,155 @@ def test_rotary_dims_supported(lib, r, hd, ok):
 BASE = 0x7F0000000000
 
 
-def _layout(L=5, nb=512, nkv=8, bs=64, hd=128, dtype=_lib.KV_AUTO, stride=None, caches=None,
-            ks=None, vs=None):
-    esize = 1 if dtype == _lib.KV_FP8_E4M3 else 2
-    stride = stride if stride is not None else nb * nkv * bs * 2 * hd * esize + 4096
+def _tensor(data, shape, dtype, strides=None, on_gpu=1, device=0, dtype_name=None):
+    t = _lib.TensorInfo()
+    t.data = data
+    t.dtype = dtype
+    t.dtype_name = dtype_name.encode() if dtype_name else None
+    t.on_gpu = on_gpu
+    t.device_index = device
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    t.shape[:len(shape)] = list(shape)
+    t.strides[:len(shape)] = list(strides)
+    return t
+
+
+def _layers(L=5, nb=512, nkv=8, bs=64, kv="auto", stride=None, caches=None, ks=None, vs=None):
+    """LayerInfo records of L caches [nb, nkv, bs, 256] at fake addresses."""
+    fp8 = kv in ("fp8", "fp8_e4m3")
+    esize = 1 if fp8 else 2
+    stride = stride if stride is not None else nb * nkv * bs * 256 * esize + 4096
     caches = caches if caches is not None else [BASE + l * stride for l in range(L)]
     ks = ks if ks is not None else [0x10000 + 8 * l for l in range(L)]
     vs = vs if vs is not None else [0x10004 + 8 * l for l in range(L)]
-    return [L, caches, ks, vs, nb, nkv, bs, hd, dtype]
+    out = []
+    for l in range(L):
+        a = _lib.LayerInfo()
+        a.kv_cache_dtype = kv.encode()
+        a.kv_cache = _tensor(caches[l], (nb, nkv, bs, 256),
+                             _lib.DTYPE_UINT8 if fp8 else _lib.DTYPE_BF16)
+        a.k_scale = _tensor(ks[l], (1,), _lib.DTYPE_FP32)
+        a.v_scale = _tensor(vs[l], (1,), _lib.DTYPE_FP32)
+        out.append(a)
+    return out
 
 
-def _validate(args):
-    st = _lib.dspark_ctx_kv_validate(*args)
+def _validate(layers, n=None):
+    st = _lib.dspark_ctx_kv_validate(len(layers) if n is None else n, layers)
     return st, _lib.dspark_ctx_kv_last_error() if st else None
 
 
 def test_validate_accepts_the_workload_layouts(lib):
-    assert _validate(_layout())[0] == _lib.OK
-    assert _validate(_layout(dtype=_lib.KV_FP8_E4M3, bs=16, nb=4096))[0] == _lib.OK
-    assert _validate(_layout(L=1, nkv=2, bs=16, nb=8))[0] == _lib.OK
+    assert _validate(_layers())[0] == _lib.OK
+    assert _validate(_layers(kv="fp8", bs=16, nb=4096))[0] == _lib.OK
+    assert _validate(_layers(kv="fp8_e4m3", bs=16, nb=4096))[0] == _lib.OK
+    assert _validate(_layers(L=1, nkv=2, bs=16, nb=8))[0] == _lib.OK
     # layers may sit below layer 0 (negative offsets)
-    assert _validate(_layout(L=3, caches=[BASE + 4096, BASE, BASE + 8192]))[0] == _lib.OK
+    assert _validate(_layers(L=3, caches=[BASE + 4096, BASE, BASE + 8192]))[0] == _lib.OK
+    # a dim of size 1 may carry any stride and still be contiguous
+    one = _layers(L=1, nb=1)
+    one[0].kv_cache.strides[0] = 12345
+    assert _validate(one)[0] == _lib.OK
 
 
-@pytest.mark.parametrize("mutate,reason", [
-    (lambda a: a.__setitem__(0, 0), "no layers"),
-    (lambda a: a.__setitem__(0, 33), "layers exceed"),
-    (lambda a: a.__setitem__(8, 7), "kv_cache_dtype 7"),
-    (lambda a: a[1].__setitem__(2, 0), "KV cache not bound"),
-    (lambda a: a.__setitem__(4, 0), "KV cache not bound"),
-    (lambda a: a.__setitem__(7, 64), "unexpected cache shape"),
-    (lambda a: a.__setitem__(6, 48), "block size 48 is not a power of two"),
-    (lambda a: a[2].__setitem__(1, 0), "_k_scale is not a device fp32 pointer"),
-    (lambda a: a[3].__setitem__(4, 0x10006), "_v_scale is not a device fp32 pointer"),
-    (lambda a: a[1].__setitem__(3, a[1][3] + 2), "not 16-element aligned to each other"),
-    (lambda a: a[1].__setitem__(0, BASE + 8), "not 16-byte aligned"),
-])
+def _set(field, value):
+    def f(layers):
+        obj, name = layers[1], field
+        for part in name.split(".")[:-1]:
+            obj = getattr(obj, part)
+        last = name.split(".")[-1]
+        if "[" in last:
+            arr, idx = last[:-1].split("[")
+            getattr(obj, arr)[int(idx)] = value
+        else:
+            setattr(obj, last, value)
+    return f
+
+
+# every reason the layout rules give, reached through the C ABI, in the
+# page's words (layer 1 broken, layer 0 fine)
+LAYOUT_REASONS = [
+    (_set("kv_cache_dtype", b"int8"), "kv_cache_dtype 'int8'"),
+    (_set("kv_cache_dtype", None), "kv_cache_dtype None"),
+    (_set("kv_cache.data", None), "KV cache not bound"),
+    (_set("kv_cache.shape[0]", 0), "KV cache not bound"),
+    (_set("kv_cache.shape[3]", 128), "unexpected cache shape (512, 8, 64, 128)"),
+    (_set("kv_cache.ndim", 3), "unexpected cache shape (512, 8, 64)"),
+    (_set("kv_cache.ndim", 1), "unexpected cache shape (512,)"),
+    (_set("kv_cache.shape[2]", 48), "block size 48 is not a power of two"),
+    (_set("kv_cache.strides[1]", 64 * 256 * 2), "cache is not contiguous"),
+    (_set("kv_cache.dtype", _lib.DTYPE_OTHER), "cache has dtype an unsupported type"),
+    (_set("k_scale.data", None), "_k_scale is not a CUDA fp32 tensor"),
+    (_set("k_scale.dtype", _lib.DTYPE_BF16), "_k_scale is not a CUDA fp32 tensor"),
+    (_set("v_scale.on_gpu", 0), "_v_scale is not a CUDA fp32 tensor"),
+    (_set("kv_cache.shape[0]", 256), "layers do not share cache shape/stride/dtype"),
+    (_set("kv_cache_dtype", b"fp8"), "fp8 cache has dtype"),
+    (_set("kv_cache.device_index", 1), "layers are on different devices"),
+    (_set("kv_cache.data", BASE + 2 * 512 * 8 * 64 * 256 * 2 + 8), "not 16-element aligned to each other"),
+    (_set("k_scale.data", 0x10002), "_k_scale of layer 1 is not 4-byte aligned"),
+]
+
+
+@pytest.mark.parametrize("mutate,reason", LAYOUT_REASONS, ids=[r for _, r in LAYOUT_REASONS])
 def test_validate_reasons(lib, mutate, reason):
-    args = _layout()
-    args[1] = list(args[1])
-    args[2] = list(args[2])
-    args[3] = list(args[3])
-    mutate(args)
-    if args[0] > len(args[1]):
-        args[1] = args[1] + [BASE] * (args[0] - len(args[1]))
-        args[2] = args[2] + [0x10000] * (args[0] - len(args[2]))
-        args[3] = args[3] + [0x10000] * (args[0] - len(args[3]))
-    st, why = _validate(args)
+    layers = _layers()
+    mutate(layers)
+    st, why = _validate(layers)
     assert st == _lib.E_LAYOUT
-    assert reason in why
+    assert reason in why, why
+
+
+def test_validate_reasons_named_by_the_framework(lib):
+    layers = _layers()
+    layers[1].kv_cache.dtype = _lib.DTYPE_OTHER
+    layers[1].kv_cache.dtype_name = b"torch.int16"
+    assert _validate(layers) == (_lib.E_LAYOUT, "cache has dtype torch.int16")
+    layers = _layers(kv="fp8")
+    layers[0].kv_cache.dtype = _lib.DTYPE_BF16
+    layers[0].kv_cache.dtype_name = b"torch.bfloat16"
+    assert _validate(layers) == (_lib.E_LAYOUT, "fp8 cache has dtype torch.bfloat16")
+
+
+def test_validate_layer_and_rule_order(lib):
+    """Layers are checked in order, each against every rule in turn: layer
+    0's later rule wins over layer 1's earlier one."""
+    layers = _layers()
+    layers[0].k_scale.data = None                  # rule 7 on layer 0
+    layers[1].kv_cache_dtype = b"int8"              # rule 1 on layer 1
+    assert _validate(layers)[1] == "_k_scale is not a CUDA fp32 tensor"
+    layers = _layers()
+    layers[1].kv_cache.shape[2] = 3                 # both block size and the shared shape
+    assert "not a power of two" in _validate(layers)[1]
+
+
+def test_validate_counts(lib):
+    assert _validate(_layers(), n=0) == (_lib.E_LAYOUT, "no layers")
+    assert _lib.load().dspark_ctx_kv_validate(3, None) == _lib.E_LAYOUT
+    assert "no layers" in _lib.dspark_ctx_kv_last_error()
+    st, why = _validate(_layers(L=33))
+    assert st == _lib.E_LAYOUT and "33 layers exceed the supported 32" in why
+    layers = _layers()
+    layers[0].kv_cache.data = BASE + 8
+    for a in layers[1:]:
+        a.kv_cache.data = a.kv_cache.data + 8
+    assert _validate(layers) == (_lib.E_LAYOUT, "layer 0 cache is not 16-byte aligned")
 
 
 def test_fp8_alignment_is_in_elements(lib):
     # 16 uint8 elements = 16 bytes apart is aligned for fp8 caches, not for bf16
     caches = [BASE, BASE + 16 * 1000]
-    assert _validate(_layout(L=2, dtype=_lib.KV_FP8_E4M3, caches=caches))[0] == _lib.OK
+    assert _validate(_layers(L=2, kv="fp8", caches=caches))[0] == _lib.OK
     caches = [BASE, BASE + 16 * 1001]
-    assert _validate(_layout(L=2, dtype=_lib.KV_AUTO, caches=caches))[0] == _lib.E_LAYOUT
+    assert _validate(_layers(L=2, kv="auto", caches=caches))[0] == _lib.E_LAYOUT
 
 
 def test_create_write_argument_checks_destroy(lib):
-    st, w = _lib.dspark_ctx_kv_writer_create(*_layout())
+    st, w = _lib.dspark_ctx_kv_writer_create(5, _layers())
     assert st == _lib.OK and w
     fake = BASE + 0x100000
     common = dict(k_norm_weight=fake, eps=1e-6, positions=fake, cos_sin_cache=fake,
@@ -164,39 +252,43 @@ def test_create_write_argument_checks_destroy(lib):
 
 
 def test_create_refuses_bad_layout_and_null_out(lib):
-    args = _layout()
-    args[6] = 3
-    st, w = _lib.dspark_ctx_kv_writer_create(*args)
+    layers = _layers()
+    layers[3].kv_cache.shape[2] = 3
+    st, w = _lib.dspark_ctx_kv_writer_create(5, layers)
     assert st == _lib.E_LAYOUT and w is None
     assert "power of two" in _lib.dspark_ctx_kv_last_error()
     L = _lib.load()
-    assert L.dspark_ctx_kv_writer_create(5, None, None, None, 1, 1, 1, 128, 0, None) == _lib.E_ARG
+    assert L.dspark_ctx_kv_writer_create(5, None, None) == _lib.E_ARG
 
 
-def test_python_writer_validate_reasons_on_cpu_tensors():
-    """The torch-level rules of _validate run without a GPU."""
+def test_python_layer_facts_on_cpu_tensors():
+    """The binding only describes the layers; the reasons come from the
+    library's rules (no GPU needed: CPU tensors are simply not on a GPU)."""
     import torch
-    from speculative_decoding_draft_02_amd.writer import AttnLayer, DSparkContextKVWriter
+    from speculative_decoding_draft_02_amd.writer import (AttnLayer, DSparkContextKVWriter,
+                                                          layout_error)
     cache = torch.zeros(4, 2, 16, 256, dtype=torch.bfloat16)
     sc = torch.ones(1)
-    V = DSparkContextKVWriter._validate
-    assert V([]) == "no layers"
-    assert V([AttnLayer(cache, sc, sc, "int8")]) == "kv_cache_dtype 'int8'"
-    assert V([AttnLayer(torch.zeros(0), sc, sc)]) == "KV cache not bound"
-    assert V([AttnLayer(torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16), sc, sc)]).startswith(
-        "unexpected cache shape")
-    assert V([AttnLayer(torch.zeros(4, 2, 12, 256, dtype=torch.bfloat16), sc, sc)]) == \
+    E = layout_error
+    assert E([]) == "no layers"
+    assert E([AttnLayer(cache, sc, sc, "int8")]) == "kv_cache_dtype 'int8'"
+    assert E([AttnLayer(cache, sc, sc, None)]) == "kv_cache_dtype None"
+    assert E([AttnLayer(torch.zeros(0), sc, sc)]) == "KV cache not bound"
+    assert E([AttnLayer(None, sc, sc)]) == "KV cache not bound"
+    assert E([AttnLayer(torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16), sc, sc)]) == \
+        "unexpected cache shape (4, 2, 16, 128)"
+    assert E([AttnLayer(torch.zeros(4, 2, 12, 256, dtype=torch.bfloat16), sc, sc)]) == \
         "block size 12 is not a power of two"
-    assert V([AttnLayer(cache.transpose(1, 2), sc, sc)]) == "cache is not contiguous"
-    assert V([AttnLayer(cache, sc, sc, "fp8")]) == "fp8 cache has dtype torch.bfloat16"
-    assert V([AttnLayer(cache.view(torch.int16), sc, sc)]) == "cache has dtype torch.int16"
-    assert V([AttnLayer(cache, sc, sc)]) == "_k_scale is not a CUDA fp32 tensor"
+    assert E([AttnLayer(cache.transpose(1, 2), sc, sc)]) == "cache is not contiguous"
+    assert E([AttnLayer(cache, sc, sc, "fp8")]) == "fp8 cache has dtype torch.bfloat16"
+    assert E([AttnLayer(cache.view(torch.int16), sc, sc)]) == "cache has dtype torch.int16"
+    assert E([AttnLayer(cache, sc, sc)]) == "_k_scale is not a CUDA fp32 tensor"
     with pytest.raises(ValueError, match="unsupported DSpark context-KV layout: no layers"):
         DSparkContextKVWriter([])
 
 
 def test_layer_slots_entry_argument_checks(lib):
-    st, w = _lib.dspark_ctx_kv_writer_create(*_layout(L=3))
+    st, w = _lib.dspark_ctx_kv_writer_create(3, _layers(L=3))
     assert st == _lib.OK
     fake = BASE + 0x100000
 
@@ -294,7 +386,7 @@ def test_hidden_norm_and_project_write_argument_checks(lib):
     assert hn(fake, 1 << 31, 512, fake, 1e-6, fake, None) == _lib.E_ARG
     assert hn(fake, 0, 512, fake, 1e-6, fake, None) == _lib.OK        # no launch
 
-    st, w = _lib.dspark_ctx_kv_writer_create(*_layout(L=2, nkv=2))
+    st, w = _lib.dspark_ctx_kv_writer_create(2, _layers(L=2, nkv=2))
     assert st == _lib.OK
 
     def pw(**kw):

@@ -245,9 +245,12 @@ def test_error_paths():
     with pytest.raises(RuntimeError, match="rotary_dim 48"):
         writer(inp.all_kv, inp.w, 1e-6, inp.positions,
                torch.zeros(64, 48, dtype=torch.bfloat16, device="cuda:0"), 48, inp.slots)
-    with pytest.raises(AssertionError):
+    with pytest.raises(RuntimeError, match="built for 2 and 2"):
         writer(inp.all_kv[:, :1].contiguous(), inp.w[:1].contiguous(), 1e-6, inp.positions,
                inp.cos_sin, 32, inp.slots)
+    with pytest.raises(ValueError, match="all_kv must be"):
+        writer(inp.all_kv[..., :64].contiguous(), inp.w, 1e-6, inp.positions, inp.cos_sin, 32,
+               inp.slots)
     with pytest.raises(ValueError, match="positions"):
         writer(inp.all_kv, inp.w, 1e-6, inp.positions.to(torch.int32), inp.cos_sin, 32, inp.slots)
     # odd block size and misaligned caches are refused at construction
@@ -263,6 +266,43 @@ def test_error_paths():
     with pytest.raises(ValueError, match="16-element aligned"):
         DSparkContextKVWriter(mis)
     assert DSparkContextKVWriter.supported(layers)
+
+
+# ---------------------------------------- positions of padding tokens --
+#
+# A token stored in no layer never has its position used as a table index,
+# so its position may lie off the table: here every such token carries -1 or
+# cos_sin_rows, and the caches must equal the oracle's (which reads no
+# position of an unstored token) on every launch path.
+PADDING_POSITION_CASES = [
+    # N, L, nkv, R, bs, blocks, fp8, pad, per-layer mappings
+    (300, 5, 8, 64, 64, 16, False, 0.3, False),    # one token per wave, one layer per wave
+    (3300, 4, 4, 64, 16, 256, True, 0.2, False),   # one token per wave, fp8 groups of 3
+    (8200, 2, 8, 64, 16, 520, False, 0.2, False),  # one token per wave, whole row groups
+    (300, 5, 2, 32, 16, 32, False, 0.5, False),    # general mapping, one layer per wave
+    (2100, 3, 3, 16, 16, 200, False, 0.3, False),  # general mapping, whole row groups
+    (3200, 9, 2, 64, 8, 512, False, 0.1, False),   # general mapping, chunks of 8 layers
+    (16, 2, 2, 32, 16, 1, False, 1.0, False),      # every token is padding
+    (300, 5, 8, 64, 64, 32, False, 0.3, True),     # per-layer, one layer per wave
+    (2100, 9, 8, 32, 16, 140, True, 0.3, True),    # per-layer, fp8 groups of 3
+    (8200, 2, 8, 64, 16, 520, False, 0.2, True),   # per-layer, whole row groups
+    (129, 3, 2, 16, 4, 80, False, 0.3, True),      # per-layer, general rows
+    (2100, 3, 3, 32, 16, 200, True, 0.3, True),    # per-layer, general rows, whole groups
+]
+
+
+@pytest.mark.parametrize("shape", PADDING_POSITION_CASES, ids=lambda s: "N%d-L%d-H%d-%s%s" % (
+    s[0], s[1], s[2], "fp8" if s[6] else "bf16", "-layer-slots" if s[8] else ""))
+def test_padding_positions_off_the_table(oracle_lib, shape):
+    N, L, nkv, R, bs, nb, fp8, pad, per_layer = shape
+    wl = W.custom(N, L, nkv, R, bs, nb, fp8, seed=31 * N + L, pad_fraction=pad,
+                  kv_std=4.0 if fp8 else 1.0)
+    if per_layer:
+        wl = W.per_layer_slots(wl, seed=N + 5, pad_fraction=0.1)
+    wl = W.padding_positions_off_table(wl)
+    off = (wl.positions < 0) | (wl.positions >= wl.cos_sin.shape[0])
+    assert off.any() or pad == 0
+    _check(oracle_lib, wl, label="padding-positions")
 
 
 # ------------------------------------------------- per-layer slot mappings --

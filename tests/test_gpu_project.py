@@ -138,6 +138,31 @@ def test_project_write_exact_grids(oracle_lib, shape, packed):
     writer.close()
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_project_write_padding_positions_off_the_table(oracle_lib, packed):
+    """Padding tokens (and the rows past num_ctx in the last tile) stage
+    cos/sin row 0, never their own position: with every padding token's
+    position at -1 or cos_sin_rows the caches still equal the oracle's."""
+    wl = W.project_exact(700, 256, 2, 4, 64, 16, 64, False, seed=77, pad_fraction=0.3)
+    wl = W.padding_positions_off_table(wl)
+    assert ((wl.positions < 0) | (wl.positions >= wl.cos_sin.shape[0])).any()
+    print("case project padding positions", "packed" if packed else "row-major", flush=True)
+    layers = _layers(wl)
+    writer = DSparkContextKVWriter(layers)
+    weight = pack_kv_weight(_bf16(wl.kv_weight)) if packed else _bf16(wl.kv_weight)
+    writer.project_write(_bf16(wl.states), weight, _bf16(wl.k_norm_weight), wl.eps,
+                         torch.from_numpy(wl.positions).to(DEV), _bf16(wl.cos_sin),
+                         wl.rotary_dim, torch.from_numpy(wl.slot_mapping).to(DEV))
+    torch.cuda.synchronize()
+    got = [_codes(a.kv_cache) for a in layers]
+    ww = wl.write_workload(oracle_lib.kv_project(wl.states, wl.kv_weight))
+    ref = oracle_lib.ctx_kv_write(ww.all_kv, ww.k_norm_weight, ww.eps, ww.positions, ww.cos_sin,
+                                  ww.rotary_dim, ww.slot_mapping, ww.new_host_caches(), False)
+    rep = C.compare(got, ref, ww.slot_mapping, False, ww.sentinel)
+    assert rep.failures == 0, rep.totals()
+    writer.close()
+
+
 def _sample_tokens(wl, count, seed):
     valid = np.flatnonzero(wl.slot_mapping >= 0)
     rng = np.random.default_rng(seed)

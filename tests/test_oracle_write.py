@@ -451,3 +451,23 @@ def test_relocated_blocks_keep_block_structure():
     assert np.array_equal(b[:, None] == b[None, :], mb[:, None] == mb[None, :])
     assert np.unique(m[m >= 0]).size == m[m >= 0].size
     assert m.max() < wl.num_blocks * wl.block_size
+
+
+@pytest.mark.parametrize("per_layer", [False, True])
+def test_padding_positions_are_never_read(oracle_lib, per_layer):
+    """A token stored in no layer contributes nothing, so moving its position
+    off the cos/sin table (-1, rows) leaves every cache byte as it was."""
+    wl = W.custom(120, 3, 2, 32, 8, 40, True, seed=9, pad_fraction=0.3, kv_std=4.0)
+    if per_layer:
+        wl = W.per_layer_slots(wl, seed=10, pad_fraction=0.1)
+    moved = W.padding_positions_off_table(wl)
+    assert (moved.positions != wl.positions).sum() >= 20
+    assert {-1, wl.cos_sin.shape[0]} <= set(moved.positions.tolist())
+    a = oracle_lib.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
+                                wl.rotary_dim, wl.slot_mapping, wl.new_host_caches(), True,
+                                wl.k_scales, wl.v_scales)
+    b = oracle_lib.ctx_kv_write(moved.all_kv, moved.k_norm_weight, moved.eps, moved.positions,
+                                moved.cos_sin, moved.rotary_dim, moved.slot_mapping,
+                                moved.new_host_caches(), True, moved.k_scales, moved.v_scales)
+    for x, y in zip(a.caches, b.caches):
+        assert np.array_equal(x, y)
