@@ -92,6 +92,30 @@ int dspark_ctx_kv_writer_project_write_packed(dspark_ctx_kv_writer *w, const voi
                                               int32_t rotary_dim, const int64_t *slot_mapping,
                                               void *stream);
 
+/* dspark_ctx_kv_writer_project_write (weight_packed == 0, kv_weight
+ * row-major) or dspark_ctx_kv_writer_project_write_packed (weight_packed ==
+ * 1, kv_weight from dspark_kv_weight_pack) that also stores the projection's
+ * bf16 output all_kv [num_ctx, num_layers, 2, num_kv_heads, 128] to
+ * all_kv_out: exactly the values the write's norm, RoPE and conversion were
+ * applied to (the token-major projection's output on the vLLM API page
+ * "vllm.models.minimax_m3.common.dspark", _project_context_kv_token_major).
+ * For callers that need all_kv itself besides the caches, and for checking
+ * the fused kernel; the store adds num_ctx * cols * 2 bytes of traffic.
+ * all_kv_out: device memory, contiguous, 16-byte aligned, not overlapping any
+ * other argument, owned by the caller.  Every other argument, precondition,
+ * cache byte and return value as for those entry points; DSPARK_E_ARG also
+ * for a NULL or misaligned all_kv_out (num_ctx > 0) or weight_packed other
+ * than 0 or 1. */
+int dspark_ctx_kv_writer_project_write_all_kv(dspark_ctx_kv_writer *w, const void *states,
+                                              int64_t num_ctx, int32_t hidden,
+                                              const void *kv_weight, int32_t weight_packed,
+                                              int32_t num_layers, int32_t num_kv_heads,
+                                              const void *k_norm_weight, float eps,
+                                              const int64_t *positions,
+                                              const void *cos_sin_cache, int64_t cos_sin_rows,
+                                              int32_t rotary_dim, const int64_t *slot_mapping,
+                                              void *all_kv_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

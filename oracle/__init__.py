@@ -298,3 +298,27 @@ def kv_project(z, W, rows=None, cols=None, want_sums: bool = False):
                                    out.ctypes.data, ex.ctypes.data if want_sums else None,
                                    ab.ctypes.data if want_sums else None)
     return (out, ex, ab) if want_sums else out
+
+
+def kv_project_sums(z, W):
+    """The projection's exact dot products for every row and column, for
+    full-size checks: z (uint16 bf16 bits [N, hidden]) and W ([C, hidden])
+    decoded to float64, where every bf16 x bf16 product is exact; the sums
+    z @ W.T and |z| @ |W|.T are taken by numpy's float64 matrix product (a
+    library primitive, any summation order).  Returns (sums, abs_sums, err)
+    with |sums - exact| <= err and |abs_sums - sum |products|| <= err
+    elementwise, err = gamma_hidden(2^-53) * abs_sums * (1 + gamma) (the
+    worst case for any order of n float64 additions of exact products)."""
+    z = np.ascontiguousarray(z, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    hidden = z.shape[1]
+    assert W.shape[1] == hidden
+
+    def decode(bits):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    zd, wd = decode(z), decode(W)
+    sums = zd @ wd.T
+    abs_sums = np.abs(zd) @ np.abs(wd).T
+    g = hidden * 2.0 ** -53 / (1.0 - hidden * 2.0 ** -53)
+    return sums, abs_sums, g * abs_sums * (1.0 + g)

@@ -273,42 +273,84 @@ def compare_insert(dev_qkv, dev_cache, dev_q_fp8, oracle_result, num_heads: int,
 #
 # With Gaussian data the device's fp32 accumulation of the projection is not
 # exact, so its bf16 all_kv may differ from the exactly rounded value.  The
-# acceptance is then an interval per stored element, derived from the
-# arithmetic and propagated through the write with interval arithmetic:
-#   * all_kv: |acc - exact| <= gamma_n * sum|z W| (n = hidden, any summation
-#     order, exact products; gamma_n = n u / (1 - n u), u = 2^-24), plus
-#     sum |W| |dz| over the hidden-norm near ties where the device may hold the
-#     other bf16 neighbour of z; bf16 rounding is monotone, so the device's
-#     value lies in [RNE(exact - b), RNE(exact + b)];
-#   * K: the norm's r over the interval box, x r (1 + w) over the corners,
-#     RoPE over the corners, each fp32 stage widened by 2^-19 relative (fp32
-#     evaluation and v_rsq_f32), then rounded to bf16 outward;
+# acceptance is then an interval per value, derived from the arithmetic:
+#   * all_kv: |acc - exact| <= b, where b bounds the fp32 summation error of
+#     the hidden-size dot product (exact bf16 x bf16 products), either in the
+#     worst case for any order (Higham, Accuracy and Stability of Numerical
+#     Algorithms, 2nd ed., eq. 3.5 and section 4.2: gamma_n sum|z W|,
+#     gamma_n = n u / (1 - n u)) or, tighter, by the probabilistic bound of
+#     Higham and Mary (SIAM J. Sci. Comput. 41(5), 2019, Theorem 3.1): with
+#     rounding errors modelled as independent and of mean zero, for any order
+#     |acc - exact| <= gamma~_n(lam) sum|z W|, gamma~_n(lam) = exp(lam sqrt(n)
+#     u + n u^2 / (1 - u)) - 1, except with probability at most
+#     2 n exp(-lam^2 (1 - u)^2 / 2) per value.  bf16 rounding is monotone, so
+#     the device's all_kv lies in [RNE(exact - b), RNE(exact + b)];
+#   * K (write_intervals): the norm's r over the interval box, x r (1 + w)
+#     over the corners, RoPE over the corners, each fp32 stage widened by
+#     2^-19 relative (fp32 evaluation and v_rsq_f32), then rounded to bf16
+#     outward;
 #   * fp8: e4m3 of value / scale is monotone, so the interval maps through.
 
-_U = 2.0 ** -24
+U32 = 2.0 ** -24            # unit roundoff of fp32
+U64 = 2.0 ** -53            # unit roundoff of fp64
 _WIDEN = 2.0 ** -19
+BF16_MIN_SUBNORMAL = 2.0 ** -133
 
 
-def _rne_bf16(x64):
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float64)).to(torch.float32)
-    return t.to(torch.bfloat16).to(torch.float64).numpy()
+def rne_bf16(x64):
+    """Each float64 value rounded once, to nearest with ties to even, onto
+    the bf16 grid (8 significant bits, exponents down to -126, subnormal step
+    2^-133), returned as float64.  Values beyond the bf16 range are not
+    expected here."""
+    x = np.asarray(x64, dtype=np.float64)
+    m, e = np.frexp(x)                        # x = m 2^e, 0.5 <= |m| < 1
+    # the grid step at x: 2^(e - 8) for normal bf16 values, 2^-133 below 2^-126
+    step_exp = np.maximum(e - 8, -133)
+    return np.ldexp(np.rint(np.ldexp(x, -step_exp)), step_exp)
+
+
+def gamma(n: int, u: float = U32) -> float:
+    """Worst-case relative error factor of n roundings: n u / (1 - n u)."""
+    return n * u / (1.0 - n * u)
+
+
+def gamma_prob(n: int, lam: float, u: float = U32) -> float:
+    """Higham and Mary's probabilistic factor gamma~_n(lam)."""
+    return float(np.expm1(lam * np.sqrt(n) * u + n * u * u / (1.0 - u)))
+
+
+def prob_bound_failure(n: int, lam: float, u: float = U32) -> float:
+    """Per-value probability that the probabilistic bound does not hold
+    (the model's union bound): 2 n exp(-lam^2 (1 - u)^2 / 2)."""
+    return float(2.0 * n * np.exp(-lam * lam * (1.0 - u) ** 2 / 2.0))
+
+
+def projection_bound(abs_sum, hidden: int, lam=None, sum_err=0.0):
+    """Bound b on |device fp32 dot product - exact| for dot products of
+    `hidden` exact products with sum of |products| abs_sum: the worst case
+    for any order when lam is None, else the probabilistic bound at lam.
+    sum_err: how far the caller's exact sums and abs_sum may themselves be
+    off (fp64 evaluation), added on top."""
+    g = gamma(hidden) if lam is None else gamma_prob(hidden, lam)
+    return g * (np.asarray(abs_sum, np.float64) + sum_err) + sum_err
+
+
+def all_kv_interval(exact, b):
+    """[lo, hi] (bf16 values as float64) that the device's bf16 all_kv must
+    lie in, given the exact dot products and the bound b."""
+    return rne_bf16(exact - b), rne_bf16(exact + b)
 
 
 def _widen(lo, hi):
     return (lo - np.abs(lo) * _WIDEN - 1e-38, hi + np.abs(hi) * _WIDEN + 1e-38)
 
 
-def write_intervals(exact, abs_sum, dz_term, hidden, k_norm_weight, cos, sin, rotary_dim, kv,
-                    eps=1e-6):
+def write_intervals(exact, b, k_norm_weight, cos, sin, rotary_dim, kv, eps=1e-6):
     """Bounds [lo, hi] (float64, bf16 values) of the stored values of one
-    all_kv row group.  exact, abs_sum, dz_term: [T, 128] for one (layer, kv,
-    head); k_norm_weight: [128] float; cos, sin: [T, R/2] float; kv 0 = K."""
-    n = float(hidden)
-    gamma = n * _U / (1.0 - n * _U)
-    b = gamma * (abs_sum + dz_term) + dz_term
-    xlo = _rne_bf16(exact - b)
-    xhi = _rne_bf16(exact + b)
+    all_kv row group.  exact, b: [T, 128] exact dot products and their error
+    bounds for one (layer, kv, head); k_norm_weight: [128] float; cos, sin:
+    [T, R/2] float; kv 0 = K."""
+    xlo, xhi = all_kv_interval(exact, b)
     if kv == 1:
         return xlo, xhi
     # the norm's r over the box: mean x^2 between the smallest and largest squares
@@ -321,7 +363,7 @@ def write_intervals(exact, abs_sum, dz_term, hidden, k_norm_weight, cos, sin, ro
     g = 1.0 + k_norm_weight[None, :]
     c = np.stack([xlo * r_lo * g, xlo * r_hi * g, xhi * r_lo * g, xhi * r_hi * g])
     ylo, yhi = _widen(c.min(axis=0), c.max(axis=0))
-    ylo, yhi = _rne_bf16(ylo), _rne_bf16(yhi)
+    ylo, yhi = rne_bf16(ylo), rne_bf16(yhi)
     R = rotary_dim
     h = R // 2
     klo, khi = ylo.copy(), yhi.copy()
@@ -338,6 +380,6 @@ def write_intervals(exact, abs_sum, dz_term, hidden, k_norm_weight, cos, sin, ro
     as_lo, as_hi = prod(a_lo, a_hi, sin)
     f_lo, f_hi = _widen(ac_lo - ps_hi, ac_hi - ps_lo)     # first half: a c - p s
     s_lo, s_hi = _widen(pc_lo + as_lo, pc_hi + as_hi)     # second half: p c + a s
-    klo[:, :h], khi[:, :h] = _rne_bf16(f_lo), _rne_bf16(f_hi)
-    klo[:, h:R], khi[:, h:R] = _rne_bf16(s_lo), _rne_bf16(s_hi)
+    klo[:, :h], khi[:, :h] = rne_bf16(f_lo), rne_bf16(f_hi)
+    klo[:, h:R], khi[:, h:R] = rne_bf16(s_lo), rne_bf16(s_hi)
     return klo, khi

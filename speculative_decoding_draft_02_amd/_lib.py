@@ -62,6 +62,9 @@ SIGNATURES = {
     "dspark_ctx_kv_writer_project_write_packed": ([_P, _P, _I64, _I32, _P, _I32, _I32, _P,
                                                    ctypes.c_float, _P, _P, _I64, _I32, _P, _P],
                                                   ctypes.c_int),
+    "dspark_ctx_kv_writer_project_write_all_kv": ([_P, _P, _I64, _I32, _P, _I32, _I32, _I32, _P,
+                                                   ctypes.c_float, _P, _P, _I64, _I32, _P, _P,
+                                                   _P], ctypes.c_int),
     "dspark_kv_weight_pack": ([_P, _I64, _I32, _P, _P], ctypes.c_int),
     "dspark_qknorm_rope_kv_insert": ([_P, _I64, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                       ctypes.c_float, _P, _P, _I64, _I32, _I32, _P, _P, _P,
@@ -169,6 +172,17 @@ def dspark_ctx_kv_writer_project_write_packed(writer, states, num_ctx, hidden, p
     return load().dspark_ctx_kv_writer_project_write_packed(
         writer, states, num_ctx, hidden, packed_kv_weight, num_layers, num_kv_heads, k_norm_weight,
         eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping, stream)
+
+
+def dspark_ctx_kv_writer_project_write_all_kv(writer, states, num_ctx, hidden, kv_weight,
+                                              weight_packed, num_layers, num_kv_heads,
+                                              k_norm_weight, eps, positions, cos_sin_cache,
+                                              cos_sin_rows, rotary_dim, slot_mapping, all_kv_out,
+                                              stream) -> int:
+    return load().dspark_ctx_kv_writer_project_write_all_kv(
+        writer, states, num_ctx, hidden, kv_weight, weight_packed, num_layers, num_kv_heads,
+        k_norm_weight, eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim, slot_mapping,
+        all_kv_out, stream)
 
 
 def dspark_kv_weight_pack(kv_weight, cols, hidden, packed, stream) -> int:

@@ -49,7 +49,8 @@ int project_write(dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, 
                   const void *kv_weight, int32_t num_layers, int32_t num_kv_heads,
                   const void *k_norm_weight, float eps, const int64_t *positions,
                   const void *cos_sin_cache, int64_t cos_sin_rows, int32_t rotary_dim,
-                  const int64_t *slot_mapping, void *stream, bool packed) {
+                  const int64_t *slot_mapping, void *stream, bool packed,
+                  void *all_kv_out = nullptr) {
     if (w == nullptr)
         return fail(DSPARK_E_ARG, "writer is NULL");
     if (num_layers != w->num_layers || num_kv_heads != w->num_kv_heads)
@@ -80,6 +81,8 @@ int project_write(dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, 
     if ((num_ctx + 256) * hidden * 2 >= (int64_t{1} << 31) || cols * hidden * 2 >= (int64_t{1} << 31))
         return fail(DSPARK_E_ARG, "states or kv_weight exceed 2 GiB (num_ctx %lld, hidden %d)",
                     (long long)num_ctx, hidden);
+    if (all_kv_out != nullptr && !aligned(all_kv_out, 16))
+        return fail(DSPARK_E_ARG, "all_kv_out must be 16-byte aligned");
     if (num_ctx == 0)
         return DSPARK_OK;
 
@@ -93,6 +96,7 @@ int project_write(dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, 
     a.slots = slot_mapping;
     a.cache0 = w->cache0;
     a.scale0 = w->scale0;
+    a.all_kv_out = static_cast<uint16_t *>(all_kv_out);
     a.num_ctx = static_cast<uint32_t>(num_ctx);
     a.hidden = hidden;
     a.cols = static_cast<uint32_t>(cols);
@@ -131,6 +135,21 @@ extern "C" int dspark_ctx_kv_writer_project_write_packed(
     return project_write(w, states, num_ctx, hidden, packed_kv_weight, num_layers, num_kv_heads,
                          k_norm_weight, eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim,
                          slot_mapping, stream, true);
+}
+
+extern "C" int dspark_ctx_kv_writer_project_write_all_kv(
+    dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, int32_t hidden,
+    const void *kv_weight, int32_t weight_packed, int32_t num_layers, int32_t num_kv_heads,
+    const void *k_norm_weight, float eps, const int64_t *positions, const void *cos_sin_cache,
+    int64_t cos_sin_rows, int32_t rotary_dim, const int64_t *slot_mapping, void *all_kv_out,
+    void *stream) {
+    if (weight_packed != 0 && weight_packed != 1)
+        return fail(DSPARK_E_ARG, "weight_packed must be 0 or 1, not %d", weight_packed);
+    if (all_kv_out == nullptr && num_ctx > 0)
+        return fail(DSPARK_E_ARG, "all_kv_out is NULL");
+    return project_write(w, states, num_ctx, hidden, kv_weight, num_layers, num_kv_heads,
+                         k_norm_weight, eps, positions, cos_sin_cache, cos_sin_rows, rotary_dim,
+                         slot_mapping, stream, weight_packed == 1, all_kv_out);
 }
 
 extern "C" int dspark_kv_weight_pack(const void *kv_weight, int64_t cols, int32_t hidden,

@@ -22,6 +22,8 @@ struct ProjArgs {
     const int64_t *slots;          // [num_ctx], < 0 = padding
     void *cache0;                  // layer 0's cache (bf16 or uint8 elements)
     const float *scale0;           // layer 0's k scale
+    uint16_t *all_kv_out;          // bf16 [num_ctx, cols]: the projection's output,
+                                   // also stored when not NULL
     uint32_t num_ctx;
     int32_t hidden;                // multiple of 64
     uint32_t cols;                 // L * 2 * nkv * 128

@@ -150,8 +150,8 @@ __device__ __forceinline__ float round_bf16(float v) { return bf16_lo(pack_bf16(
 // the main loop must be complete before the call.
 template <int R, bool kFp8, int WM, int WN, int TI, int kBM, class TileRow>
 __device__ __forceinline__ void project_epilogue(const ProjArgs &a, f32x16 (&acc)[TI][4],
-                                                 uint32_t nb, int wn, int wrow, int tid,
-                                                 int lane, int64_t my_pos,
+                                                 int64_t m0, uint32_t nb, int wn, int wrow,
+                                                 int tid, int lane, int64_t my_pos,
                                                  const int64_t (&my_slot)[TI / 2],
                                                  uint16_t *cs_lds, TileRow tile_row) {
     // this wave's 128 columns are all_kv's (layer, kv, head) = a row of the write
@@ -208,6 +208,17 @@ __device__ __forceinline__ void project_epilogue(const ProjArgs &a, f32x16 (&acc
         for (int n = 0; n < 4; ++n)
 #pragma unroll
             for (int e = 0; e < 16; ++e) y[n][e] = round_bf16(acc[i][n][e]);
+        if (a.all_kv_out != nullptr && m0 + rho < a.num_ctx) {
+            // the projection's bf16 output itself: runs of 4 columns
+            uint16_t *orow = a.all_kv_out + (m0 + rho) * a.cols + head * DSPARK_HEAD_DIM + 4 * hi;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2 *>(orow + 32 * n + 8 * q) =
+                        make_uint2(pack_bf16(y[n][4 * q], y[n][4 * q + 1]),
+                                   pack_bf16(y[n][4 * q + 2], y[n][4 * q + 3]));
+        }
         if (kv == 0) {
             float ss = 0.0f;
 #pragma unroll
@@ -532,7 +543,7 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
     __syncthreads();
 
     project_epilogue<R, kFp8, WM, WN, TI, kBM>(
-        a, acc, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(st4),
+        a, acc, m0, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(st4),
         [&](int row) {
             constexpr int kRowBytes = kFp8 ? 128 : 256;
             constexpr int kRowsPerStage = kDStage * 16 / kRowBytes;
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
     // stages
     uint8_t *const sp = reinterpret_cast<uint8_t *>(spare);
     project_epilogue<R, kFp8, WM, WN, TI, kBM>(
-        a, acc, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(spare),
+        a, acc, m0, nb, wn, wrow, tid, lane, my_pos, my_slot, reinterpret_cast<uint16_t *>(spare),
         [&](int row) {
             constexpr int kRowBytes = kFp8 ? 128 : 256;
             constexpr int kCsBytes = kBM * 64 * 2;

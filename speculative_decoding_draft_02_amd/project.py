@@ -58,10 +58,12 @@ def precompute_and_store_context_kv(writer: DSparkContextKVWriter, context_state
                                     k_norm_weight: torch.Tensor,
                                     positions: torch.Tensor, cos_sin_cache: torch.Tensor,
                                     rotary_dim: int, slot_mapping: torch.Tensor,
-                                    workspace: torch.Tensor | None = None) -> None:
+                                    workspace: torch.Tensor | None = None,
+                                    all_kv_out: torch.Tensor | None = None) -> None:
     """hidden_norm(context_states) into `workspace` (allocated when None),
     then the projection with every draft layer's context write fused in
-    (kv_weight row-major, or packed by pack_kv_weight)."""
+    (kv_weight row-major, or packed by pack_kv_weight); all_kv_out, if given,
+    also receives the projection's bf16 output [num_ctx, L, 2, nkv, 128]."""
     z = hidden_norm(context_states, hidden_norm_weight, eps, out=workspace)
     writer.project_write(z, kv_weight, k_norm_weight, eps, positions, cos_sin_cache, rotary_dim,
-                         slot_mapping)
+                         slot_mapping, all_kv_out=all_kv_out)

@@ -257,13 +257,16 @@ class DSparkContextKVWriter:
     def project_write(self, states: torch.Tensor, kv_weight: "torch.Tensor | PackedKVWeight",
                       k_norm_weight: torch.Tensor, eps: float, positions: torch.Tensor,
                       cos_sin_cache: torch.Tensor, rotary_dim: int,
-                      slot_mapping: torch.Tensor) -> None:
+                      slot_mapping: torch.Tensor, all_kv_out: "torch.Tensor | None" = None) -> None:
         """The projection all_kv = states @ kv_weight.T with this write fused
-        into its epilogue (all_kv is never stored).  states: bf16
-        [num_ctx, hidden], the hidden-norm output; kv_weight: bf16
-        [L * 2 * nkv * 128, hidden] ([out, in], rows in all_kv's order), or
-        that weight packed by project.pack_kv_weight (same results, bit for
-        bit); slot_mapping: one int64 [num_ctx] tensor shared by every layer."""
+        into its epilogue (all_kv is not stored unless all_kv_out is given).
+        states: bf16 [num_ctx, hidden], the hidden-norm output; kv_weight:
+        bf16 [L * 2 * nkv * 128, hidden] ([out, in], rows in all_kv's order),
+        or that weight packed by project.pack_kv_weight (same results, bit
+        for bit); slot_mapping: one int64 [num_ctx] tensor shared by every
+        layer; all_kv_out: an optional bf16 [num_ctx, L, 2, nkv, 128] tensor
+        that also receives the projection's output (the values the write
+        normalised and stored)."""
         L, nkv = self._num_layers, self._num_kv_heads
         dev = self._layers[0].kv_cache.device
         if states.dim() != 2:
@@ -290,6 +293,11 @@ class DSparkContextKVWriter:
             raise ValueError("positions and slot_mapping must have shape (num_ctx,)")
         if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != rotary_dim:
             raise ValueError(f"cos_sin_cache has shape {tuple(cos_sin_cache.shape)}")
+        if all_kv_out is not None:
+            self._check_inputs(num_ctx, (("all_kv_out", all_kv_out, torch.bfloat16),), ())
+            if tuple(all_kv_out.shape) != (num_ctx, L, 2, nkv, HEAD_DIM):
+                raise ValueError(f"all_kv_out has shape {tuple(all_kv_out.shape)}, "
+                                 f"expected {(num_ctx, L, 2, nkv, HEAD_DIM)}")
         if num_ctx == 0:
             return
         self._bind()
@@ -298,12 +306,19 @@ class DSparkContextKVWriter:
             check_write_preconditions(positions, slot_mapping, cos_sin_cache.shape[0],
                                       c0.shape[0], c0.shape[2])
         stream = torch.cuda.current_stream(dev).cuda_stream
-        fn = (_lib.dspark_ctx_kv_writer_project_write_packed if packed
-              else _lib.dspark_ctx_kv_writer_project_write)
-        st = fn(
-            self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(), L, nkv,
-            k_norm_weight.data_ptr(), float(eps), positions.data_ptr(), cos_sin_cache.data_ptr(),
-            cos_sin_cache.shape[0], int(rotary_dim), slot_mapping.data_ptr(), stream)
+        if all_kv_out is not None:
+            st = _lib.dspark_ctx_kv_writer_project_write_all_kv(
+                self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(),
+                int(packed), L, nkv, k_norm_weight.data_ptr(), float(eps), positions.data_ptr(),
+                cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(rotary_dim),
+                slot_mapping.data_ptr(), all_kv_out.data_ptr(), stream)
+        else:
+            fn = (_lib.dspark_ctx_kv_writer_project_write_packed if packed
+                  else _lib.dspark_ctx_kv_writer_project_write)
+            st = fn(self._handle, states.data_ptr(), num_ctx, hidden, kv_weight.data_ptr(), L,
+                    nkv, k_norm_weight.data_ptr(), float(eps), positions.data_ptr(),
+                    cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(rotary_dim),
+                    slot_mapping.data_ptr(), stream)
         if st != _lib.OK:
             raise RuntimeError("DSpark projection + context-KV write failed: "
                                + _lib.dspark_ctx_kv_last_error())

@@ -416,6 +416,25 @@ def test_hidden_norm_and_project_write_argument_checks(lib):
         assert pw(**kw) == _lib.E_ARG, kw
         assert reason in E(), (kw, E())
     assert pw(num_ctx=0) == _lib.OK                                    # no launch
+
+    def pwkv(**kw):
+        a = dict(writer=w, states=fake, num_ctx=300, hidden=512, kv_weight=fake,
+                 weight_packed=0, num_layers=2, num_kv_heads=2, k_norm_weight=fake, eps=1e-6,
+                 positions=fake, cos_sin_cache=fake, cos_sin_rows=4096, rotary_dim=64,
+                 slot_mapping=fake, all_kv_out=fake, stream=None)
+        a.update(kw)
+        return _lib.dspark_ctx_kv_writer_project_write_all_kv(*a.values())
+
+    for kw, reason in [
+        (dict(weight_packed=2), "weight_packed must be 0 or 1"),
+        (dict(all_kv_out=None), "all_kv_out is NULL"),
+        (dict(all_kv_out=fake + 8), "all_kv_out must be 16-byte aligned"),
+        (dict(num_layers=3), "built for 2 and 2"),
+        (dict(weight_packed=1, hidden=96), "multiple of 64"),
+    ]:
+        assert pwkv(**kw) == _lib.E_ARG, kw
+        assert reason in E(), (kw, E())
+    assert pwkv(num_ctx=0, all_kv_out=None) == _lib.OK                 # no launch
     _lib.dspark_ctx_kv_writer_destroy(w)
 
 
