@@ -119,10 +119,15 @@ class Setup:
         else:
             self._write = lib.dspark_ctx_kv_writer_write
             slot_args = [i["slots"].data_ptr() for i in self.inputs]
-        self._args = [(self.handle, i["all_kv"].data_ptr(), wl.num_ctx, wl.num_layers,
-                       wl.num_kv_heads, i["w"].data_ptr(), wl.eps, i["positions"].data_ptr(),
-                       i["cos_sin"].data_ptr(), i["cos_sin"].shape[0], wl.rotary_dim, sa)
-                      for i, sa in zip(self.inputs, slot_args)]
+        # every set passes its own token count (sets of one workload may
+        # differ in it: the decode batches draw the tokens per request)
+        for st in self.sets:
+            assert (st.num_layers, st.num_kv_heads, st.cache_shape, st.fp8) == \
+                (wl.num_layers, wl.num_kv_heads, wl.cache_shape, wl.fp8)
+        self._args = [(self.handle, i["all_kv"].data_ptr(), st.num_ctx, st.num_layers,
+                       st.num_kv_heads, i["w"].data_ptr(), st.eps, i["positions"].data_ptr(),
+                       i["cos_sin"].data_ptr(), i["cos_sin"].shape[0], st.rotary_dim, sa)
+                      for st, i, sa in zip(self.sets, self.inputs, slot_args)]
 
     def launch(self, k: int, stream_ptr) -> None:
         """One write of input set k % n through the C ABI (the same tensors
@@ -162,7 +167,10 @@ class InsertSetup:
         self.token_layers = [s.num_tokens for s in self.sets]
         lib = _lib.load()
         self._call = lib.dspark_qknorm_rope_kv_insert
-        self._args = [(i["qkv"].data_ptr(), wl.num_tokens, self.qw.data_ptr(), self.kw.data_ptr(),
+        for st in self.sets:       # one cache and one set of weights serve every set
+            assert (st.num_heads, st.num_kv_heads, st.cache_shape, st.fp8, st.rotary_dim) == \
+                (wl.num_heads, wl.num_kv_heads, wl.cache_shape, wl.fp8, wl.rotary_dim)
+        self._args = [(i["qkv"].data_ptr(), st.num_tokens, self.qw.data_ptr(), self.kw.data_ptr(),
                        self.cs.data_ptr(), self.cs.shape[0], i["positions"].data_ptr(),
                        wl.num_heads, wl.num_kv_heads, wl.rotary_dim, wl.eps,
                        i["slots"].data_ptr(), self.cache.data_ptr(), wl.num_blocks,
@@ -170,7 +178,7 @@ class InsertSetup:
                        self.ks.data_ptr() if wl.fp8 else None,
                        self.vs.data_ptr() if wl.fp8 else None,
                        i["qf"].data_ptr() if i["qf"] is not None else None, wl.q_scale)
-                      for i in self.inputs]
+                      for st, i in zip(self.sets, self.inputs)]
 
     def launch(self, k: int, stream_ptr) -> None:
         st = self._call(*self._args[k % len(self._args)], stream_ptr)
@@ -178,15 +186,36 @@ class InsertSetup:
             raise RuntimeError(_lib.dspark_ctx_kv_last_error())
 
 
+# The GPU's clock settles over the first ~20 ms of sustained work, so every
+# timed region is preceded by at least this much back-to-back work of the
+# same launch, whatever --warmup says (--warmup sets the minimum number of
+# warm-up calls); the timed region itself is exactly --steps launches.
+WARMUP_FLOOR_S = 0.2
+
+
+def warm_up(launch, calls: int, floor_s: float = WARMUP_FLOOR_S) -> int:
+    """At least `calls` calls of launch(k) and at least floor_s seconds of
+    them (checked every 64 calls at a synchronisation point); returns the
+    number of calls made."""
+    k = 0
+    t0 = time.perf_counter()
+    while k < calls or time.perf_counter() - t0 < floor_s:
+        launch(k)
+        k += 1
+        if k % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return k
+
+
 def time_eager(setup: Setup, steps: int, warmup: int, stream):
-    """Warm up, then time exactly `steps` back-to-back launches with one HIP
-    event pair around the region on the launch stream.  A second, untimed
-    pass with an event pair around every launch gives the spread of single
-    kernel durations."""
+    """Warm up (warm_up), then time exactly `steps` back-to-back launches
+    with one HIP event pair around the region on the launch stream.  A
+    second, untimed pass with an event pair around every launch gives the
+    spread of single kernel durations."""
     sp = stream.cuda_stream
     with torch.cuda.stream(stream):
-        for k in range(warmup):
-            setup.launch(k, sp)
+        warmup = warm_up(lambda k: setup.launch(k, sp), warmup)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -223,8 +252,7 @@ def time_graph(setup, steps: int, warmup: int, stream, per_graph: int = 50):
             sp = torch.cuda.current_stream().cuda_stream
             for k in range(per_graph):
                 setup.launch(k, sp)
-        for _ in range(max(1, warmup // per_graph)):
-            g.replay()
+        warm_up(lambda k: g.replay(), max(1, warmup // per_graph))
         replays = max(1, steps // per_graph)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -485,52 +513,82 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(index: int, budget_s: float = 12.0):
-    """The oracle on this host's cores, on whole calls of the workload (test
-    infrastructure: only this leg of the bench uses it).  Single-threaded,
-    then with one contiguous token range per thread (the oracle's C code runs
-    with the GIL released), each timed over repeated whole calls for about
-    budget_s / 2 seconds."""
+# the box this bench runs on allots 16 CPUs to each GPU: the oracle's
+# all-core leg uses at most that many threads
+CPU_THREAD_CAP = 16
+
+
+def token_prefix(wl, n: int):
+    """The workload's first n tokens (same caches, tables and weights)."""
+    import dataclasses
+    return dataclasses.replace(wl, num_ctx=n, all_kv=wl.all_kv[:n], positions=wl.positions[:n],
+                               slot_mapping=wl.slot_mapping[..., :n])
+
+
+def cpu_baseline(target_s: float = 1.0):
+    """The oracle (plain C in fp64 with near-tie tracking; test
+    infrastructure: only this leg of the bench uses it) on this host's
+    cores, per workload, on a bounded sample: the workload's first tokens,
+    as many as one single-threaded pass covers in about target_s (the whole
+    call when it is smaller), timed single-threaded and with one contiguous
+    token range per thread (its C code runs with the GIL released), best of
+    3 runs each; rates are the sample's algorithmic bytes and token-layers
+    over its time.  Reported as a baseline for context, not as a target."""
     sys.path.insert(0, ROOT)
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     oracle.build()
-    wl = W.make(index)
-    caches = wl.new_host_caches()
-
-    def run(t_begin, t_end):
-        oracle.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions, wl.cos_sin,
-                            wl.rotary_dim, wl.slot_mapping, caches, wl.fp8, wl.k_scales,
-                            wl.v_scales, t_begin=t_begin, t_end=t_end)
-
-    def timed(threads):
-        bounds = np.linspace(0, wl.num_ctx, threads + 1).astype(int)
-        reps, total = 0, 0.0
-        with ThreadPoolExecutor(threads) as ex:
-            while reps == 0 or total < budget_s / 2:
-                t0 = time.perf_counter()
-                list(ex.map(lambda i: run(bounds[i], bounds[i + 1]), range(threads)))
-                total += time.perf_counter() - t0
-                reps += 1
-        return reps, total
-
     try:
-        ncores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        ncores = os.cpu_count() or 1
-    threads = max(1, min(16, ncores))
-    r1, t1 = timed(1)
-    rn, tn = timed(threads)
-    b = wl.algorithmic_bytes()
-    return {"value": b * rn / tn / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d whole call(s) of the %s workload (%d tokens) on %d threads, one "
-                      "contiguous token range each, %.1f s; CPU %s"
-                      % (rn, wl.name, wl.num_ctx, threads, tn, cpu_model()),
-            "token_layers_per_s": wl.token_layers() * rn / tn,
-            "single_thread": {"value": b * r1 / t1 / 1e9, "unit": "GB/s", "cores": 1,
-                              "sample": "%d whole call(s), %.1f s" % (r1, t1),
-                              "token_layers_per_s": wl.token_layers() * r1 / t1}}
+        avail = os.cpu_count() or 1
+    threads = max(1, min(CPU_THREAD_CAP, avail))
+    per = {}
+    for index, name in enumerate(W.NAMES):
+        full = W.make(index)
+
+        def timed(wl, n_threads, runs):
+            caches = wl.new_host_caches()
+            bounds = np.linspace(0, wl.num_ctx, n_threads + 1).astype(int)
+
+            def run(i):
+                oracle.ctx_kv_write(wl.all_kv, wl.k_norm_weight, wl.eps, wl.positions,
+                                    wl.cos_sin, wl.rotary_dim, wl.slot_mapping, caches, wl.fp8,
+                                    wl.k_scales, wl.v_scales, t_begin=bounds[i],
+                                    t_end=bounds[i + 1])
+            ts = []
+            with ThreadPoolExecutor(n_threads) as ex:
+                for _ in range(runs):
+                    t0 = time.perf_counter()
+                    list(ex.map(run, range(n_threads)))
+                    ts.append(time.perf_counter() - t0)
+            return min(ts)
+
+        probe = min(full.num_ctx, 64)
+        per_token = timed(token_prefix(full, probe), 1, 1) / probe
+        n = int(min(full.num_ctx, max(probe, target_s / max(per_token, 1e-9))))
+        wl = token_prefix(full, n)
+        t1, tn = timed(wl, 1, 3), timed(wl, threads, 3)
+        b, tl = wl.algorithmic_bytes(), wl.token_layers()
+        per[name] = {"sample_tokens": n, "of_tokens": full.num_ctx,
+                     "single_thread_GB_s": b / t1 / 1e9, "all_threads_GB_s": b / tn / 1e9,
+                     "single_thread_token_layers_per_s": tl / t1,
+                     "all_threads_token_layers_per_s": tl / tn,
+                     "single_thread_s": t1, "all_threads_s": tn, "threads": threads}
+        log("cpu baseline", name, json.dumps(per[name]))
+    h = per[W.NAMES[HEADLINE]]
+    return {"value": h["all_threads_GB_s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "prefill_bf16's first %d of %d tokens (the headline; every workload's "
+                      "sample under per_workload), best of 3 runs on %d threads, one contiguous "
+                      "token range each; single-threaded figures alongside"
+                      % (h["sample_tokens"], h["of_tokens"], threads),
+            "host_cores": os.cpu_count(), "cores_available": avail,
+            "thread_cap": "%d threads: the CPU share of one GPU on the measuring box"
+                          % CPU_THREAD_CAP,
+            "cpu": cpu_model(),
+            "single_thread": {"value": h["single_thread_GB_s"], "unit": "GB/s", "cores": 1},
+            "per_workload": per}
 
 
 def traffic_for(name: str):
@@ -546,6 +604,48 @@ def traffic_for(name: str):
     return rec.get("bytes_per_launch")
 
 
+# The launch each measured workload takes (ctx_kv_kernel.hip, launch_one:
+# one wave per 4 (token, kv head) rows and per layer or group of layers).
+KERNELS = {
+    "prefill_bf16": "ctx_kv_write_kernel<R=64, bf16 cache, one layer per wave, 4 heads of one "
+                    "token per wave>",
+    "prefill_fp8": "ctx_kv_write_kernel<R=64, e4m3 cache, groups of 3 layers per wave, 4 heads "
+                   "of one token per wave>",
+    "long_fp8": "ctx_kv_write_kernel<R=32, e4m3 cache, groups of 3 layers per wave, 4 heads of "
+                "one token per wave>",
+    "decode_bf16": "ctx_kv_write_kernel<R=16, bf16 cache, one layer per wave, 4 heads of one "
+                   "token per wave> under HIP-graph replay",
+    "prefill_bf16_layer_slots": "ctx_kv_write_kernel<R=64, bf16 cache, per-layer slots, one "
+                                "layer per wave>",
+    "prefill_bf16_tp4_shard": "ctx_kv_write_kernel<R=64, bf16 cache, general row mapping "
+                              "(nkv = 2), every layer of a row group in one wave>",
+    "project_prefill_bf16": "project_write_kernel<R=64, bf16 cache> (row-major weight)",
+    "project_prefill_fp8": "project_write_kernel<R=64, e4m3 cache> (row-major weight)",
+    "insert_draft_bf16": "qknorm_insert_kernel<R=64, bf16 cache>",
+    "insert_draft_fp8": "qknorm_insert_kernel<R=64, e4m3 cache, q fp8>",
+}
+
+
+def roofline_entry(name: str, r: dict):
+    """The roofline block of one measured workload: the dominant kernel's
+    algorithmic bytes (or flops) per launch over its average launch
+    duration in the timed region, against the MI355X's published peak."""
+    if "project_write_TFLOP_s" in r:
+        return {"bound": "mfma", "achieved": r["project_write_TFLOP_s"],
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": r["project_write_TFLOP_s"] / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                "kernel": KERNELS.get(name, name), "kernel_us_avg": r["project_write_us"],
+                "algorithmic_flops_per_launch": r["gemm_flops"]}
+    gbs = r.get("kernel_GB_s", r.get("GB_s"))
+    if gbs is None:
+        return None
+    us = r.get("kernel_us_avg", r.get("us_per_call"))
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for(name),
+            "kernel": KERNELS.get(name, name), "kernel_us_avg": us,
+            "algorithmic_bytes_per_launch": r.get("bytes_per_call")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,7 +653,9 @@ def main():
     # untimed calls before each timed region: the GPU's clock settles over
     # the first ~20 ms of sustained work (an fp8 prefill timed after 20 calls
     # read 27.8 us, after another ~9 ms of calls 24.9 us, then 23.7 us)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="minimum warm-up calls before each timed region (at least %.0f ms "
+                         "of launches are made in any case)" % (WARMUP_FLOOR_S * 1e3))
     ap.add_argument("--workload", default="all", choices=["all", "insert", "project"] + W.NAMES)
     ap.add_argument("--insert-sets", type=int, default=32,
                     help="draft blocks rotated in the insert's graph")
@@ -779,7 +881,11 @@ def main():
     head = W.NAMES[HEADLINE]
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "warmup_policy": "at least --warmup calls and at least %.0f ms of back-to-back "
+                            "launches of the same workload before each timed region; the "
+                            "timed region is exactly --steps launches" % (WARMUP_FLOOR_S * 1e3)}
+    rooflines = {n: roofline_entry(n, r) for n, r in results.items()}
     if head in results:
         h = results[head]
         out.update({"value": h["GB_s"], "ms_per_step": h["ms_per_step"],
@@ -788,13 +894,9 @@ def main():
         out["config"] = {"workload": head + ": " + W.DESCRIPTIONS[HEADLINE],
                          "num_ctx": 4096, "layers": 5, "kv_heads": 8, "head_dim": 128,
                          "rotary_dim": 64, "cache": "bf16", "io": "bf16 in, bf16 cache",
+                         "arithmetic": "fp32 norm and RoPE, bf16 rounding of each result",
                          "input_sets_rotated": h["input_sets"]}
-        out["roofline"] = {"bound": "hbm", "achieved": h["kernel_GB_s"], "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": h["kernel_GB_s"] / HBM_PEAK_GBS,
-                           "traffic": traffic_for(head),
-                           "kernel": "ctx_kv_write_kernel<R=64, bf16 cache, one layer per wave, uniform token>",
-                           "kernel_us_avg": h["kernel_us_avg"],
-                           "algorithmic_bytes_per_launch": h["bytes_per_call"]}
+        out["roofline"] = dict(rooflines[head])
     else:
         name = next(iter(results))
         r0 = results[name]
@@ -804,14 +906,14 @@ def main():
         desc = (W.DESCRIPTIONS[W.NAMES.index(name)] if name in W.NAMES
                 else results[name].get("config", ""))
         out["config"] = {"workload": name + ": " + desc}
-        out["roofline"] = None
+        out["roofline"] = dict(rooflines[name]) if rooflines.get(name) else {}
+    # every measured workload's roofline, next to the headline's
+    out["roofline"]["per_workload"] = {n: r for n, r in rooflines.items() if r is not None}
     out["workloads"] = results
     out["reference_copy"] = reference_copy
-    ctx_names = [n for n in results if n in W.NAMES]
-    if not args.no_cpu_baseline and ctx_names:
+    if not args.no_cpu_baseline and any(n in W.NAMES for n in results):
         log("cpu baseline (oracle)")
-        cb_index = HEADLINE if head in results else W.NAMES.index(ctx_names[0])
-        out["cpu_baseline"] = cpu_baseline(cb_index)
+        out["cpu_baseline"] = cpu_baseline()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

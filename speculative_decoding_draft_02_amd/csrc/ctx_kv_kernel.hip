@@ -114,6 +114,14 @@ constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SL
 constexpr int kGroupLayersBf16 = DSPARK_GROUP_LAYERS_BF16;
 constexpr int kGroupLayersFp8 = DSPARK_GROUP_LAYERS_FP8;
 constexpr int kGroupLayersGeneral = DSPARK_GROUP_LAYERS_GENERAL;
+#ifndef DSPARK_SLOT_FIRST
+#define DSPARK_SLOT_FIRST 1
+#endif
+// Split launches with one token per wave test the token's slot (or its
+// slots, with per-layer mappings) before issuing the row loads, so a
+// padding token's rows are not read; other launches issue the loads ahead
+// of the slot.
+constexpr bool kSlotFirst = DSPARK_SLOT_FIRST;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
@@ -172,6 +180,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     int64_t slot, pos;
     uint4 dk[kChunk], dv[kChunk], wv[kChunk];
     int64_t lslot[kChunk];          // per-layer slots (kLayerSlots only)
+    // the slots are read and tested before the rows (split, one token per wave)
+    constexpr bool kSlotsFirst = kSlotFirst && kLayerSplit && kUniform;
     bool in_range = true;
     const int64_t kv_stride = static_cast<int64_t>(nkv) * 16;    // K_l -> V_l (uint4 units)
     const uint4 *w_base = reinterpret_cast<const uint4 *>(a.k_norm_weight) + l0 * 16 + c;
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             dk[j] = load_row16(kv_base + (2 * l) * kv_stride);
             dv[j] = load_row16(kv_base + (2 * l + 1) * kv_stride);
             wv[j] = w_base[l * 16];
-            if constexpr (kLayerSlots) lslot[j] = a.layer_slots[l0 + l][t];
+            if constexpr (kLayerSlots && !kSlotsFirst) lslot[j] = a.layer_slots[l0 + l][t];
         }
     };
     // per-layer mappings: whether token t has a slot >= 0 in any of the
@@ -209,10 +219,23 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
                   ((static_cast<int64_t>(t) * Lrow + l0) * 2 * nkv + h) * 16 + c;
         slot = kLayerSlots ? 0 : a.slots[t];    // per-layer slots: read per layer
         pos = a.positions[t];
-        // The row loads do not depend on the slot: they go out together with
-        // the slot load, so the slot's latency overlaps theirs (a padding
-        // token's rows are then read for nothing).  The barrier keeps the
-        // compiler from sinking them below the padding exit.
+        if constexpr (kSlotsFirst) {
+            // one layer group per wave: the slot (read by every layer group's
+            // wave of this row group, mostly from L2) is tested before any
+            // row is read
+            if constexpr (kLayerSlots) {
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j)
+                    lslot[j] = a.layer_slots[l0 + (j < L ? j : L - 1)][t];
+                if (!stored_in_any_layer()) return;
+            } else if (slot < 0 || pos < 0) {
+                return;
+            }
+        }
+        // Otherwise the row loads go out together with the slot load, so the
+        // slot's latency overlaps theirs (a padding token's rows are then
+        // read for nothing).  The barrier keeps the compiler from sinking
+        // them below the padding exit.
         load_chunk(0);
         asm volatile("" ::: "memory");
         // padding: nothing written (a negative position never occurs; testing
