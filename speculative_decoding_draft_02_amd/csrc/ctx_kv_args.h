@@ -26,7 +26,13 @@ struct CtxKvArgs {
     int32_t nkv;
     int32_t bs_log2;             // log2(block_size)
     float eps;
-    int32_t pad_;
+    // reciprocal multipliers ceil(2^32 / d) for the wave -> (row group, layer
+    // group) split (d = layer groups) and, with 4 heads of one token per
+    // wave, for wave -> token (d = nkv / 4); 0 = divide (see fast_div)
+    uint32_t split_magic;
+    uint32_t token_magic;
+    float zero;                  // 0.0f, read as a wave-uniform value
+    int32_t xcd_remap;           // give each XCD a contiguous run of workgroups
     int64_t cache_off[DSPARK_MAX_LAYERS];  // elements from cache0
     int64_t kscale_off[DSPARK_MAX_LAYERS]; // floats from scale0
     int64_t vscale_off[DSPARK_MAX_LAYERS]; // floats from scale0

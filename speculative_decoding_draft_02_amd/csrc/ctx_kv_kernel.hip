@@ -101,12 +101,14 @@ constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SL
 // fp8 prefill 25.0 -> 23.8 us at 8192 waves, -4.2% at 6144, -1.6% at 4096,
 // long fp8 181.8 -> 176.7 us, per-layer slots fp8 -3.4%; bf16 -2.4% at 65536
 // waves and even at 32768; the general mapping 6% slower (bf16, nkv = 2,
-// 2048 waves) and even for fp8.  Groups of two were mixed.
+// 2048 waves) and even for fp8.  fp8 takes groups of two ({0,1}, {2,3},
+// {4}): with the XCD remap kept for large launches only, the fp8 prefill
+// 23.59 -> 23.12 us against groups of three, long fp8 even (177.0 vs 176.4).
 #ifndef DSPARK_GROUP_LAYERS_BF16
 #define DSPARK_GROUP_LAYERS_BF16 3
 #endif
 #ifndef DSPARK_GROUP_LAYERS_FP8
-#define DSPARK_GROUP_LAYERS_FP8 3
+#define DSPARK_GROUP_LAYERS_FP8 2
 #endif
 #ifndef DSPARK_GROUP_LAYERS_GENERAL
 #define DSPARK_GROUP_LAYERS_GENERAL 1
@@ -114,6 +116,12 @@ constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SL
 constexpr int kGroupLayersBf16 = DSPARK_GROUP_LAYERS_BF16;
 constexpr int kGroupLayersFp8 = DSPARK_GROUP_LAYERS_FP8;
 constexpr int kGroupLayersGeneral = DSPARK_GROUP_LAYERS_GENERAL;
+#ifndef DSPARK_FASTDIV
+#define DSPARK_FASTDIV 1
+#endif
+#ifndef DSPARK_DOT2_SZERO
+#define DSPARK_DOT2_SZERO 0
+#endif
 #ifndef DSPARK_SLOT_FIRST
 #define DSPARK_SLOT_FIRST 1
 #endif
@@ -127,6 +135,15 @@ constexpr int kMaxChunk = 8;   // layers held in registers at once
 // Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
 // of rows.
 constexpr bool kXcdRemap = true;
+#ifndef DSPARK_REMAP_MIN_GROUPS
+#define DSPARK_REMAP_MIN_GROUPS 8192
+#endif
+// Launches of fewer workgroups than this keep the hardware's round-robin
+// order over the XCDs.  Without the remap (medians of 7 alternating rounds):
+// fp8 prefill (4096 groups) -1.4%, decode (375) -3%, TP-4 shard -2.2%,
+// per-layer fp8 prefill -1.5%; bf16 prefill (10240) +0.8%, long fp8
+// (32768) +2.6%.
+constexpr uint32_t kRemapMinGroups = DSPARK_REMAP_MIN_GROUPS;
 constexpr int kNumXcds = 8;
 
 // kChunk = layers held in registers per pass; kSinglePass: L == kChunk (the
@@ -143,6 +160,14 @@ constexpr int kNumXcds = 8;
 // an ng-th of the loads and arithmetic, so more of them are in flight at
 // different phases.  One layer per wave up to the thresholds below, groups
 // of three beyond.
+// n / d for the wave-uniform index n: one multiply-high by the host's
+// ceil(2^32 / d) when it is exact for every n of the launch (the host
+// checks n d < 2^32), else a division.
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, uint32_t d, uint32_t magic) {
+    if (DSPARK_FASTDIV && magic != 0) return __umulhi(n, magic);
+    return d == 1 ? n : n / d;
+}
+
 template <int R, bool kFp8, int kChunk, bool kSinglePass, bool kUniform, bool kLayerSlots,
           bool kLayerSplit, int kWavesPerBlock>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const CtxKvArgs a) {
@@ -155,7 +180,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     const int nkv = a.nkv;
 
     uint32_t block = blockIdx.x;
-    if constexpr (kXcdRemap) {
+    if (kXcdRemap && a.xcd_remap) {
         // blocks [0, full) are remapped so that XCD x owns one contiguous run
         const uint32_t full = gridDim.x - gridDim.x % kNumXcds;
         if (block < full) block = (block % kNumXcds) * (full / kNumXcds) + block / kNumXcds;
@@ -167,8 +192,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         // wave w writes layer group w % ng (kChunk layers, the last one
         // shorter) of row group w / ng
         const uint32_t ng = (static_cast<uint32_t>(a.num_layers) + kChunk - 1) / kChunk;
-        l0 = static_cast<int>(wave % ng) * kChunk;
-        wave /= ng;
+        const uint32_t rg = fast_div(wave, ng, a.split_magic);
+        l0 = static_cast<int>(wave - rg * ng) * kChunk;
+        wave = rg;
         L = a.num_layers - l0 < kChunk ? a.num_layers - l0 : kChunk;
     }
     const uint32_t unit0 = wave * kRowsPerWave;             // first row of the wave
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         return any;
     };
     if constexpr (kUniform) {
-        t = unit0 / static_cast<uint32_t>(nkv);
+        t = fast_div(wave, static_cast<uint32_t>(nkv) / kRowsPerWave, a.token_magic);
         hu = static_cast<int>(unit0 - t * static_cast<uint32_t>(nkv));
         h = hu + q;
         kv_base = reinterpret_cast<const uint4 *>(a.all_kv) +
@@ -332,7 +358,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             const int l = lb + j;
             if (l >= L) break;
             uint32_t kb[4];
-            norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb);
+            norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb,
+                         DSPARK_DOT2_SZERO ? a.zero : 0.0f);
             // element index of this lane's row start (chunk excluded) in layer l
             int64_t rbase = a.cache_off[l0 + l] + row - c * 8;
             bool store = true;
@@ -430,9 +457,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
 }
 
 template <int R, bool kFp8, int kChunk, bool kSinglePass, int kWavesPerBlock>
-void launch_wpb(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
+void launch_wpb(const CtxKvArgs &args, uint32_t waves, hipStream_t stream) {
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const dim3 block(64 * kWavesPerBlock);
+    CtxKvArgs a = args;
+    a.xcd_remap = grid.x >= kRemapMinGroups;
     if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, true, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
@@ -447,13 +476,23 @@ void launch_wpb(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
 }
 
+// ceil(2^32 / d) if n_max * d < 2^32 (then n / d == umulhi(n, magic) for
+// every n <= n_max), else 0.
+uint32_t div_magic(uint64_t n_max, uint64_t d) {
+    if (d < 2 || (n_max + 1) * d >= (uint64_t{1} << 32)) return 0;
+    return static_cast<uint32_t>(((uint64_t{1} << 32) + d - 1) / d);
+}
+
 // One wave per (row group, group of kGroup layers), four waves per workgroup.
 template <int R, bool kFp8, int kGroup>
-void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
+void launch_split(const CtxKvArgs &args, uint32_t waves, hipStream_t stream) {
+    CtxKvArgs a = args;
     const uint32_t ng = (static_cast<uint32_t>(a.num_layers) + kGroup - 1) / kGroup;
     const uint32_t split = waves * ng;
+    a.split_magic = div_magic(uint64_t{split} + 3, ng);
     const dim3 grid((split + 3) / 4);
     const dim3 block(256);
+    a.xcd_remap = grid.x >= kRemapMinGroups;
     if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, true, true, true, 4>),
                            grid, block, 0, stream, a);
@@ -469,8 +508,11 @@ void launch_split(const CtxKvArgs &a, uint32_t waves, hipStream_t stream) {
 }
 
 template <int R, bool kFp8, int kChunk, bool kSinglePass>
-void launch_one(const CtxKvArgs &a, hipStream_t stream) {
+void launch_one(const CtxKvArgs &args, hipStream_t stream) {
+    CtxKvArgs a = args;
     const uint32_t waves = (a.num_units + kRowsPerWave - 1) / kRowsPerWave;
+    if (a.nkv % kRowsPerWave == 0)
+        a.token_magic = div_magic(waves, static_cast<uint32_t>(a.nkv) / kRowsPerWave);
     const bool general = !a.layer_slots_on && a.nkv % kRowsPerWave != 0;
     const uint32_t max_split =
         a.layer_slots_on ? (kFp8 ? kSplitMaxWavesLayerSlotsFp8 : kSplitMaxWavesLayerSlotsBf16)

@@ -169,7 +169,10 @@ __device__ __forceinline__ uint2 pack_fp8(const uint32_t (&b)[4], float s, float
         v[2 * k] = div_by_scale(bf16_lo(b[k]), s, y, lim);
         v[2 * k + 1] = div_by_scale(bf16_hi(b[k]), s, y, lim);
     }
-    int w0 = 0, w1 = 0;
+    // the first conversion of each word sets its low half; the high half it
+    // keeps from `old` is overwritten by the second, so `old` is any value
+    // already in a register (no zeroing move)
+    int w0 = __builtin_bit_cast(int, v[0]), w1 = __builtin_bit_cast(int, v[4]);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], w0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], w1, false);
@@ -182,7 +185,8 @@ __device__ __forceinline__ uint2 pack_fp8(const uint32_t (&b)[4], float s, float
 // half of the rotated dims), or (1, 0) on lanes past the rotated dims.
 template <int R>
 __device__ __forceinline__ void norm_rope(const uint4 &d, const uint4 &w, float eps, int c,
-                                          const uint32_t (&cs)[8], uint32_t (&out)[4]) {
+                                          const uint32_t (&cs)[8], uint32_t (&out)[4],
+                                          float zero = 0.0f) {
     constexpr int kRotLanes = R / 8;   // lanes holding rotated dims
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -206,8 +210,8 @@ __device__ __forceinline__ void norm_rope(const uint4 &d, const uint4 &w, float 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t pb = rope_partner<R>(yb[k], c);
-        const float r0 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x05040100u), cs[2 * k], 0.0f);
-        const float r1 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x07060302u), cs[2 * k + 1], 0.0f);
+        const float r0 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x05040100u), cs[2 * k], zero);
+        const float r1 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x07060302u), cs[2 * k + 1], zero);
         out[k] = (c < kRotLanes) ? pack_bf16(r0, r1) : yb[k];
     }
 }

@@ -73,7 +73,7 @@ SWEEP = [
     (2100, 3, 3, 16, 16, 200, False, 0.2),
     (3200, 9, 2, 64, 8, 512, False, 0.1),   # L > 8 in chunks
     (4200, 12, 3, 32, 4, 1200, True, 0.1),  # L > 8 in chunks, fp8
-    (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8: groups of 3 layers
+    (3300, 4, 4, 64, 16, 256, True, 0.05),  # uniform rows, fp8: groups of 2 layers
     (3300, 3, 4, 32, 16, 256, True, 0.05),  # uniform rows, fp8, L = 3: one wave per row group
     # one token per wave beyond 16384 waves: bf16 in one wave per row group
     # (L = 2) and in groups of 3 layers (L = 9)
@@ -92,14 +92,14 @@ def test_sweep_parity(oracle_lib, shape):
 
 
 # the largest supported shapes: DSPARK_MAX_LAYERS layers (one wave per
-# layer, groups of three layers per wave, and whole row groups per wave in
+# layer, groups of two (fp8) or three (bf16) layers per wave, and whole row groups per wave in
 # chunks of 8 layers), many kv heads, a large block
 MAX_CASES = [
     # N, L, nkv, R, bs, blocks, fp8, pad
     (40, 32, 2, 64, 16, 4, False, 0.1),     # per-layer split
     (40, 32, 2, 32, 16, 4, True, 0.1),
     (1600, 32, 4, 16, 64, 32, False, 0.05),  # 1600 waves, bf16: one layer per wave
-    (1600, 32, 4, 16, 64, 32, True, 0.05),   # ... fp8: eleven groups of 3 layers
+    (1600, 32, 4, 16, 64, 32, True, 0.05),   # ... fp8: sixteen groups of 2 layers
     (3200, 32, 2, 32, 64, 64, False, 0.05),  # general mapping, 1600 waves: chunks of 8
     (50, 2, 64, 64, 16, 8, True, 0.1),      # 64 kv heads
     (300, 2, 2, 32, 2048, 2, False, 0.1),   # 2048-token blocks
@@ -177,7 +177,7 @@ def test_graph_capture_replays_match_eager(oracle_lib):
     is read at replay time."""
     wl = W.make(4)
     wl2 = W.custom(100, 5, 4, 16, 128, 512, True, seed=9, pad_fraction=0.25)
-    # 1700 fp8 waves: the launch with groups of three layers per wave
+    # 1700 fp8 waves: the launch with groups of two layers per wave
     wl3 = W.custom(1700, 5, 4, 32, 128, 512, True, seed=10, pad_fraction=0.05)
     for w in (wl, wl2, wl3):
         print("case graph", w.name, w.fp8, flush=True)
@@ -277,14 +277,14 @@ def test_error_paths():
 PADDING_POSITION_CASES = [
     # N, L, nkv, R, bs, blocks, fp8, pad, per-layer mappings
     (300, 5, 8, 64, 64, 16, False, 0.3, False),    # one token per wave, one layer per wave
-    (3300, 4, 4, 64, 16, 256, True, 0.2, False),   # one token per wave, fp8 groups of 3
+    (3300, 4, 4, 64, 16, 256, True, 0.2, False),   # one token per wave, fp8 groups of 2
     (8200, 2, 8, 64, 16, 520, False, 0.2, False),  # one token per wave, whole row groups
     (300, 5, 2, 32, 16, 32, False, 0.5, False),    # general mapping, one layer per wave
     (2100, 3, 3, 16, 16, 200, False, 0.3, False),  # general mapping, whole row groups
     (3200, 9, 2, 64, 8, 512, False, 0.1, False),   # general mapping, chunks of 8 layers
     (16, 2, 2, 32, 16, 1, False, 1.0, False),      # every token is padding
     (300, 5, 8, 64, 64, 32, False, 0.3, True),     # per-layer, one layer per wave
-    (2100, 9, 8, 32, 16, 140, True, 0.3, True),    # per-layer, fp8 groups of 3
+    (2100, 9, 8, 32, 16, 140, True, 0.3, True),    # per-layer, fp8 groups of 2
     (8200, 2, 8, 64, 16, 520, False, 0.2, True),   # per-layer, whole row groups
     (129, 3, 2, 16, 4, 80, False, 0.3, True),      # per-layer, general rows
     (2100, 3, 3, 32, 16, 200, True, 0.3, True),    # per-layer, general rows, whole groups
@@ -314,7 +314,7 @@ LAYER_SLOT_CASES = [
     (129, 3, 2, 16, 4, 80, False),
     (65, 9, 3, 64, 8, 32, True),       # L > 8: chunked pass
     (257, 4, 5, 32, 128, 8, False),
-    # beyond the one-layer split: groups of 3 layers (fp8, L = 9) and whole
+    # beyond the one-layer split: groups of 2 layers (fp8, L = 9) and whole
     # row groups (bf16, L = 2)
     (2100, 9, 8, 32, 16, 140, True),   # more than 4096 waves
     (8200, 2, 8, 64, 16, 520, False),  # more than 16384 waves
