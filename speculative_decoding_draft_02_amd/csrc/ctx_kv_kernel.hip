@@ -27,8 +27,8 @@
 //   * the 128-wide sum of squares is reduced inside the 16-lane row with four
 //     DPP adds (no LDS); every lane ends with the same bits;
 //   * the RoPE partner of element i (i + R/2) sits in the same register of
-//     lane c ^ (R/16), fetched with one DPP move (R = 16, 32) or ds_swizzle
-//     (R = 64);
+//     lane c ^ (R/16), fetched with one DPP move (R = 16, 32) or two DPP
+//     row rotations and a select (R = 64);
 //   * the token's cos/sin values are loaded once per row into registers and
 //     reused for every layer;
 //   * fp8: x / scale is formed from y = RN(1/scale) (one IEEE division per
