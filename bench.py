@@ -193,10 +193,11 @@ class InsertSetup:
 WARMUP_FLOOR_S = 0.2
 
 
-def warm_up(launch, calls: int, floor_s: float = WARMUP_FLOOR_S) -> int:
-    """At least `calls` calls of launch(k) and at least floor_s seconds of
-    them (checked every 64 calls at a synchronisation point); returns the
-    number of calls made."""
+def warm_up(launch, calls: int, floor_s: float = None) -> int:
+    """At least `calls` calls of launch(k) and at least floor_s seconds
+    (default WARMUP_FLOOR_S) of them (checked every 64 calls at a
+    synchronisation point); returns the number of calls made."""
+    floor_s = WARMUP_FLOOR_S if floor_s is None else floor_s
     k = 0
     t0 = time.perf_counter()
     while k < calls or time.perf_counter() - t0 < floor_s:
@@ -647,6 +648,7 @@ def roofline_entry(name: str, r: dict):
 
 
 def main():
+    global WARMUP_FLOOR_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -656,6 +658,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000,
                     help="minimum warm-up calls before each timed region (at least %.0f ms "
                          "of launches are made in any case)" % (WARMUP_FLOOR_S * 1e3))
+    ap.add_argument("--warmup-floor-ms", type=float, default=WARMUP_FLOOR_S * 1e3,
+                    help="minimum milliseconds of launches before each timed region (counter "
+                         "runs, which serialise every launch, set 0)")
     ap.add_argument("--workload", default="all", choices=["all", "insert", "project"] + W.NAMES)
     ap.add_argument("--insert-sets", type=int, default=32,
                     help="draft blocks rotated in the insert's graph")
@@ -666,6 +671,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
+    WARMUP_FLOOR_S = max(0.0, args.warmup_floor_ms) / 1e3
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the write is "
@@ -883,8 +889,9 @@ def main():
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "warmup_policy": "at least --warmup calls and at least %.0f ms of back-to-back "
-                            "launches of the same workload before each timed region; the "
-                            "timed region is exactly --steps launches" % (WARMUP_FLOOR_S * 1e3)}
+                            "launches of the same workload before each timed region "
+                            "(--warmup-floor-ms); the timed region is exactly --steps launches"
+                            % (WARMUP_FLOOR_S * 1e3)}
     rooflines = {n: roofline_entry(n, r) for n, r in results.items()}
     if head in results:
         h = results[head]
