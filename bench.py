@@ -191,6 +191,8 @@ class InsertSetup:
 # same launch, whatever --warmup says (--warmup sets the minimum number of
 # warm-up calls); the timed region itself is exactly --steps launches.
 WARMUP_FLOOR_S = 0.2
+# untimed launches queued between the synchronisation and the start event
+PREROLL = 4
 
 
 def warm_up(launch, calls: int, floor_s: float = None) -> int:
@@ -221,6 +223,11 @@ def time_eager(setup: Setup, steps: int, warmup: int, stream):
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        # untimed launches queued ahead of the start event: the region starts
+        # on a busy GPU, so the host's latency to its first launch is not in it
+        for k in range(PREROLL):
+            setup.launch(warmup + k, sp)
+        warmup += PREROLL
         start.record(stream)
         for k in range(steps):
             setup.launch(warmup + k, sp)
@@ -258,6 +265,7 @@ def time_graph(setup, steps: int, warmup: int, stream, per_graph: int = 50):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        g.replay()          # untimed, queued ahead of the start event
         start.record(stream)
         for _ in range(replays):
             g.replay()
@@ -890,8 +898,10 @@ def main():
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "warmup_policy": "at least --warmup calls and at least %.0f ms of back-to-back "
                             "launches of the same workload before each timed region "
-                            "(--warmup-floor-ms); the timed region is exactly --steps launches"
-                            % (WARMUP_FLOOR_S * 1e3)}
+                            "(--warmup-floor-ms); after the synchronisation that opens the "
+                            "region, %d untimed launches are queued ahead of the start event so "
+                            "that the region starts on a busy GPU; the timed region is exactly "
+                            "--steps launches" % (WARMUP_FLOOR_S * 1e3, PREROLL)}
     rooflines = {n: roofline_entry(n, r) for n, r in results.items()}
     if head in results:
         h = results[head]
