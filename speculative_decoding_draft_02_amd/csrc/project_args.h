@@ -31,7 +31,9 @@ struct ProjArgs {
     int32_t nkv;
     int32_t bs_log2;
     float eps;
-    int32_t pad_;
+    uint32_t big_tiles;            // 128 x 512 tiles of a launch whose other
+                                   // workgroups take 64-token halves (set by
+                                   // the launcher)
     int64_t cache_off[DSPARK_MAX_LAYERS];   // elements from cache0
     int64_t kscale_off[DSPARK_MAX_LAYERS];  // floats from scale0
     int64_t vscale_off[DSPARK_MAX_LAYERS];  // floats from scale0

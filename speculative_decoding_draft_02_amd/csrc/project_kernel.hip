@@ -15,8 +15,9 @@
 // v_mfma_f32_32x32x16_bf16 (lane l holds A[l % 32][8 (l / 32) + i] and
 // B[8 (l / 32) + i][l % 32], i < 8; accumulator register i holds
 // D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).  A workgroup of 4 waves (one per
-// SIMD) owns a 256-token x 256-column tile; each wave computes 128 tokens x
-// 128 columns, and 128 columns are exactly one (layer, kv, head) row of
+// SIMD) owns a 256-token x 256-column tile (with a packed weight, mostly
+// 128 tokens x 512 columns); each wave computes 128 tokens x 128 columns,
+// and 128 columns are exactly one (layer, kv, head) row of
 // all_kv, so the write's per-row norm, RoPE and store happen on data the wave
 // holds.  The weight is the MFMA's first operand, so a lane ends with one
 // token's values in runs of 4 consecutive columns (half of the head; lane
@@ -31,6 +32,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "device_common.h"
 #include "project_args.h"
@@ -328,10 +331,11 @@ constexpr int kDRows = 256;              // tile rows of each operand
 constexpr int kDStage = 2 * kDRows * kDK / 8;   // 16-byte chunks: A then B
 constexpr int kDLoads = 8;               // DMA instructions per thread per stage
 constexpr int kNSt = 5;                  // stages in the ring
-// tiles in groups of kGroupM token blocks (columns vary between groups):
-// the 32 tiles an XCD runs at once span 4 token and 8 column blocks, so its
-// L2 serves 12 operand slices per k stage (18 in token-block-first order)
-constexpr uint32_t kGroupM = 4;
+// tiles in groups of kGroupTokens / kBM token blocks (columns vary between
+// groups): the 32 tiles an XCD runs at once span 1024 tokens and 2048 weight
+// columns (4 x 8 tiles of 256 x 256, or 8 x 4 of 128 x 512), so its L2 serves
+// 12 operand slices of 256 rows per k stage (18 in token-block-first order)
+constexpr uint32_t kGroupTokens = 1024;
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
 // left at their maxima).  A stage's loads go out in two halves of kDLoads / 2
 // (token rows, then weight rows a half stage later); a stage waits for its
@@ -343,24 +347,35 @@ constexpr int kWaitPrologue = vmcnt_imm((kNSt - 2) * kDLoads + kDLoads / 2);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The tile of this workgroup: 256 tokens (block mb) x 256 columns (block
-// nb).  Workgroup i runs on XCD i % 8, so XCD x takes a contiguous run of
-// the grouped tile order (kGroupM token blocks per group, columns varying
-// between groups).
+// Tiles of kBM tokens (block mb) x kBN columns (block nb), in a grouped
+// order: kGroupTokens / kBM token blocks per group, columns varying between
+// groups.
 struct Tile {
     uint32_t mb, nb;
 };
 
-__device__ __forceinline__ Tile tile_of(uint32_t num_ctx, uint32_t cols) {
-    const uint32_t mblocks = (num_ctx + kDRows - 1) / kDRows;
-    uint32_t bid = blockIdx.x;
-    const uint32_t full = gridDim.x - gridDim.x % kPNumXcds;
-    if (bid < full) bid = (bid % kPNumXcds) * (full / kPNumXcds) + bid / kPNumXcds;
-    const uint32_t gsz = kGroupM * (cols / 256);
-    const uint32_t gm0 = (bid / gsz) * kGroupM;
-    const uint32_t gm = mblocks - gm0 < kGroupM ? mblocks - gm0 : kGroupM;
-    const uint32_t rem = bid % gsz;
+template <int kBM, int kBN>
+__device__ __forceinline__ Tile tile_at(uint32_t p, uint32_t num_ctx, uint32_t cols) {
+    constexpr uint32_t kGm = kGroupTokens / kBM;
+    const uint32_t mblocks = (num_ctx + kBM - 1) / kBM;
+    const uint32_t gsz = kGm * (cols / kBN);
+    const uint32_t gm0 = (p / gsz) * kGm;
+    const uint32_t gm = mblocks - gm0 < kGm ? mblocks - gm0 : kGm;
+    const uint32_t rem = p % gsz;
     return Tile{gm0 + rem % gm, rem / gm};
+}
+
+// Workgroup i of a run of n runs on XCD i % 8; its position in the order is
+// chosen so that each XCD takes a contiguous part of the run (the last n % 8
+// keep theirs).
+__device__ __forceinline__ uint32_t xcd_run(uint32_t i, uint32_t n) {
+    const uint32_t full = n - n % kPNumXcds;
+    return i < full ? (i % kPNumXcds) * (full / kPNumXcds) + i / kPNumXcds : i;
+}
+
+template <int kBM, int kBN>
+__device__ __forceinline__ Tile tile_of(uint32_t num_ctx, uint32_t cols) {
+    return tile_at<kBM, kBN>(xcd_run(blockIdx.x, gridDim.x), num_ctx, cols);
 }
 
 // 16 bytes per lane from a buffer resource (voff per lane, soff per wave)
@@ -388,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv % WM;
     const int wn = wv / WM;
-    const Tile tile = tile_of(a.num_ctx, a.cols);
+    const Tile tile = tile_of<kBM, 128 * WN>(a.num_ctx, a.cols);
     const uint32_t nb = tile.nb;
     const int64_t m0 = static_cast<int64_t>(tile.mb) * kBM;
     const int64_t n0 = static_cast<int64_t>(nb) * (128 * WN);
@@ -555,50 +570,61 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
 
 // ------------------------------ the projection with a pre-packed weight --
 //
-// The same tile, waves, MFMAs and epilogue as above, with the weight in the
+// The same waves, MFMAs and epilogue as above, with the weight in the
 // fragment-major layout that pack_kv_weight_kernel writes: every 32 x 16
 // weight fragment of the MFMA is 1 KB contiguous, lane l's 16 bytes at
 // 16 l.  A wave then loads its weight fragments straight into registers,
 // 1 KB per instruction in whole cache lines, and the weight never passes
-// through LDS: per stage the CU's LDS moves 48 KB instead of 96 KB, and the
-// L2 serves the weight in 128-byte lines instead of 64-byte halves.  The
-// token rows still go through LDS by DMA, in a ring of four 16 KB stages;
-// the weight goes through a ring of four register stages (32 registers
-// each).  The two waves that share a weight column block both load it.
-constexpr int kPkStage = kDRows * kDK / 8;   // 16-byte chunks of a token stage (16 KB)
+// through LDS; the L2 serves it in 128-byte lines instead of 64-byte halves.
+// The token rows still go through LDS by DMA, in a ring of four stages; the
+// weight goes through a ring of four register stages (32 registers each).
+// Two arrangements of the four waves (WM x WN, each wave 128 tokens x 128
+// columns):
+//   1 x 4: 128 tokens x 512 columns (four heads) per workgroup; the token
+//          rows (8 KB per stage) are shared by the four waves, and each wave
+//          loads its own head's weight, so no fragment is fetched twice: per
+//          stage the CU moves 40 KB from L2 and 40 KB through LDS;
+//   2 x 2: 256 tokens x 256 columns, for column counts that are not a
+//          multiple of 512; the two waves that share a column block both
+//          load it (48 KB from L2 and 48 KB through LDS per stage).
+constexpr int kLdsChunks = 160 * 1024 / 16;   // the CU's LDS in 16-byte chunks
 constexpr int kPkRing = 4;                   // stages in flight, in LDS and in registers
-constexpr int kPkSpare = (10 - kPkRing) * kPkStage;   // the rest of 160 KB, for the epilogue
 // Per stage a wave issues kPkBLoads weight loads, then (after the barrier)
-// kPkALoads token loads; with a ring of n stages the token loads of stage
+// kALoads token loads; with a ring of n stages the token loads of stage
 // j + 1 are followed in issue order by the weight loads of stages j + 1 ..
 // j + n - 1 and the token loads of j + 2 .. j + n - 1 (the steady-state
 // wait).  The prologue waits for stage 0 with one more token stage in
 // flight; the last stages wait as if every weight load after the awaited
 // token loads were gone (they are dead there, and the compiler may drop
 // them).
-constexpr int kPkALoads = 4, kPkBLoads = 8;
-constexpr int kPkWaitStage = vmcnt_imm((kPkRing - 1) * kPkBLoads + (kPkRing - 2) * kPkALoads);
-constexpr int kPkWaitPrologue = vmcnt_imm((kPkRing - 1) * (kPkBLoads + kPkALoads));
-constexpr int kPkWaitTail = vmcnt_imm((kPkRing - 2) * kPkALoads);
-static_assert((kPkRing - 1) * (kPkBLoads + kPkALoads) <= 63, "vmcnt holds at most 63");
+constexpr int kPkBLoads = 8;
 
-template <int R, bool kFp8>
-__global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const ProjArgs a) {
-    constexpr int WM = 2, WN = 2, TI = 4, kBM = kDRows;
-    // four token stages, then 96 KB that hold a fifth stage (for a ring of
-    // five) and the epilogue's spare area
-    __shared__ u32x4 sa0[kPkStage], sa1[kPkStage], sa2[kPkStage], sa3[kPkStage], rest[6 * kPkStage];
+// One tile: kBM = 32 TI WM tokens from m0 by 128 WN columns of column block
+// nb.  sa0 .. sa3 are the workgroup's token stages (kStageAlloc chunks each,
+// of which a stage uses kBM * kDK / 8) and rest the remainder of its 160 KB
+// of LDS: a fifth stage (for a ring of five) and the epilogue's spare area.
+template <int R, bool kFp8, int WM, int TI, int kStageAlloc>
+__device__ __forceinline__ void packed_tile(const ProjArgs &a, int64_t m0, uint32_t nb,
+                                            u32x4 *sa0, u32x4 *sa1, u32x4 *sa2, u32x4 *sa3,
+                                            u32x4 *rest) {
+    constexpr int WN = 4 / WM, kBM = 32 * TI * WM;
+    static_assert(TI == 2 || TI == 4, "32 TI tokens per wave");
+    constexpr int kStage = kBM * kDK / 8;        // 16-byte chunks of a token stage
+    static_assert(kStage <= kStageAlloc, "a stage fits its array");
+    constexpr int kALoads = kBM / 64;            // token DMA instructions per wave and stage
+    constexpr int kWaitStage = vmcnt_imm((kPkRing - 1) * kPkBLoads + (kPkRing - 2) * kALoads);
+    constexpr int kWaitPrologue = vmcnt_imm((kPkRing - 1) * (kPkBLoads + kALoads));
+    constexpr int kWaitTail = vmcnt_imm((kPkRing - 2) * kALoads);
+    static_assert((kPkRing - 1) * (kPkBLoads + kALoads) <= 63, "vmcnt holds at most 63");
+    constexpr int kSpare = kLdsChunks - kPkRing * kStageAlloc;
     static_assert(kPkRing == 4 || kPkRing == 5, "the ring's arrays");
     u32x4 *const sa4 = rest;
-    u32x4 *const spare = rest + (kPkRing - 4) * kPkStage;
+    u32x4 *const spare = rest + (kPkRing - 4) * kStageAlloc;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv % WM;
     const int wn = wv / WM;
-    const Tile tile = tile_of(a.num_ctx, a.cols);
-    const uint32_t nb = tile.nb;
-    const int64_t m0 = static_cast<int64_t>(tile.mb) * kBM;
     const int64_t n0 = static_cast<int64_t>(nb) * (128 * WN);
 
     const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
@@ -617,7 +643,7 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
     auto issue_a = [&](u32x4 *st, int kt) {
         const int ko = kt * (kDK * 2);
 #pragma unroll
-        for (int p = 0; p < kPkALoads; ++p)
+        for (int p = 0; p < kALoads; ++p)
             dma16(zres, st + (64 * p + 16 * wv) * 4, zoff, p * pstep + ko);
     };
 
@@ -683,26 +709,20 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
                 acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][s][n], fa[s][i],
                                                                     acc[i][n], 0, 0, 0);
     };
-    // per group of four MFMAs: one LDS read and two (k step 0: the weight
-    // loads) or one (k step 1: the token loads) memory loads
-    auto interleave0 = [&]() {
+    // per group of TI MFMAs (a quarter of a k step): one LDS read (in TI of
+    // the four groups) and two (k step 0: the weight loads) or, in kALoads
+    // of the four groups, one (k step 1: the token loads) memory loads
+    auto interleave = [&](bool step0) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (g < TI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-    };
-    auto interleave1 = [&]() {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (step0)
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            else if (g % (4 / kALoads) == 0)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (TI > 2) __builtin_amdgcn_sched_group_barrier(0x008, TI - 2, 0);
         }
     };
     // Stage kt (token stage cur, weight slot `slot`): k step 0's MFMAs run
@@ -714,17 +734,17 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
         read_frags(1, cur, xs1);
         issue_b((slot + kPkRing - 1) % kPkRing, clamp(kt + kPkRing - 1));
         mfmas(slot, 0);
-        interleave0();
+        interleave(true);
         if (last)
-            __builtin_amdgcn_s_waitcnt(kPkWaitTail);
+            __builtin_amdgcn_s_waitcnt(kWaitTail);
         else
-            __builtin_amdgcn_s_waitcnt(kPkWaitStage);
+            __builtin_amdgcn_s_waitcnt(kWaitStage);
         __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         issue_a(cur, clamp(kt + kPkRing));
         read_frags(0, nxt, xs0);
         mfmas(slot, 1);
-        interleave1();
+        interleave(false);
     };
 
     u32x4 *const stp[5] = {sa0, sa1, sa2, sa3, sa4};
@@ -736,7 +756,7 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
         issue_b(j, clamp(j));
     }
     issue_a(stp[kPkRing - 1], clamp(kPkRing - 1));
-    __builtin_amdgcn_s_waitcnt(kPkWaitPrologue);
+    __builtin_amdgcn_s_waitcnt(kWaitPrologue);
     __builtin_amdgcn_s_barrier();
     read_frags(0, sa0, xs0);
     // whole rounds of the rings while more than one round is left, then the
@@ -764,8 +784,9 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
         [&](int row) {
             constexpr int kRowBytes = kFp8 ? 128 : 256;
             constexpr int kCsBytes = kBM * 64 * 2;
-            constexpr int kSpareRows = (kPkSpare * 16 - kCsBytes) / kRowBytes;
-            constexpr int kStageRows = kPkStage * 16 / kRowBytes;
+            constexpr int kSpareRows = (kSpare * 16 - kCsBytes) / kRowBytes;
+            constexpr int kStageRows = kStageAlloc * 16 / kRowBytes;
+            static_assert(kCsBytes <= kSpare * 16, "the cos/sin rows fit the spare area");
             static_assert(kSpareRows + kPkRing * kStageRows >= WN * kBM, "the finished tile fits");
             if (row < kSpareRows) return sp + kCsBytes + row * kRowBytes;
             const int r = row - kSpareRows;
@@ -773,6 +794,43 @@ __global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const Proj
             u32x4 *base = q == 0 ? sa0 : q == 1 ? sa1 : q == 2 ? sa2 : q == 3 ? sa3 : sa4;
             return reinterpret_cast<uint8_t *>(base) + (r % kStageRows) * kRowBytes;
         });
+}
+
+// 2 x 2 waves on 256 x 256 tiles, for column counts that are not a multiple
+// of 512.
+template <int R, bool kFp8>
+__global__ __launch_bounds__(256, 1) void project_write_packed_kernel(const ProjArgs a) {
+    constexpr int kStage = 256 * kDK / 8;
+    __shared__ u32x4 sa0[kStage], sa1[kStage], sa2[kStage], sa3[kStage],
+        rest[kLdsChunks - 4 * kStage];
+    const Tile tile = tile_of<256, 256>(a.num_ctx, a.cols);
+    packed_tile<R, kFp8, 2, 4, kStage>(a, static_cast<int64_t>(tile.mb) * 256, tile.nb, sa0, sa1,
+                                       sa2, sa3, rest);
+}
+
+// 1 x 4 waves on 128 x 512 tiles.  The tile count rarely divides into whole
+// rounds of the CUs, and a last round that fills few of them takes as long
+// as a full one; so when the last round would fill at most half of the CUs,
+// its tiles are run as twice as many 64-token halves (the workgroups from
+// big_tiles on), one round of about half the time.
+template <int R, bool kFp8>
+__global__ __launch_bounds__(256, 1) void project_write_packed_wide_kernel(const ProjArgs a) {
+    constexpr int kStage = 128 * kDK / 8;
+    __shared__ u32x4 sa0[kStage], sa1[kStage], sa2[kStage], sa3[kStage],
+        rest[kLdsChunks - 4 * kStage];
+    const uint32_t big = a.big_tiles;
+    if (blockIdx.x < big) {
+        const Tile t = tile_at<128, 512>(xcd_run(blockIdx.x, big), a.num_ctx, a.cols);
+        packed_tile<R, kFp8, 1, 4, kStage>(a, static_cast<int64_t>(t.mb) * 128, t.nb, sa0, sa1,
+                                           sa2, sa3, rest);
+    } else {
+        // halves 2 j and 2 j + 1 of tile big + j (in the grouped order)
+        const uint32_t h = xcd_run(blockIdx.x - big, gridDim.x - big);
+        const Tile t = tile_at<128, 512>(big + h / 2, a.num_ctx, a.cols);
+        const int64_t m0 = static_cast<int64_t>(t.mb) * 128 + 64 * (h % 2);
+        if (m0 >= a.num_ctx) return;             // a half wholly past the last token
+        packed_tile<R, kFp8, 1, 2, kStage>(a, m0, t.nb, sa0, sa1, sa2, sa3, rest);
+    }
 }
 
 // The weight's fragment-major layout: element (c, k) of the [cols, hidden]
@@ -791,13 +849,43 @@ __global__ __launch_bounds__(256) void pack_kv_weight_kernel(const u32x4 *w, u32
     out[q] = w[(static_cast<uint64_t>(c) * hidden + k) / 8];
 }
 
+// The number of compute units of the current device (read once per device).
+int cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// One workgroup per tile: 256 tokens x 256 columns, or with a packed weight
+// and a column count that is a multiple of 512, 128 tokens x 512 columns
+// (the last round's tiles, when they fill at most half of the CUs, in
+// 64-token halves).
 template <int R, bool kFp8>
 void launch_pw(const ProjArgs &a, bool packed, hipStream_t stream) {
     const dim3 grid((a.num_ctx + kDRows - 1) / kDRows * (a.cols / 256));
-    if (packed)
+    if (packed && a.cols % 512 == 0) {
+        const uint32_t tiles = (a.num_ctx + 127) / 128 * (a.cols / 512);
+        const uint32_t cus = static_cast<uint32_t>(cu_count());
+        const uint32_t last = tiles % cus;
+        ProjArgs b = a;
+        b.big_tiles = last != 0 && 2 * last <= cus ? tiles - last : tiles;
+        const uint32_t groups = b.big_tiles + 2 * (tiles - b.big_tiles);
+        hipLaunchKernelGGL((project_write_packed_wide_kernel<R, kFp8>), dim3(groups), dim3(256), 0,
+                           stream, b);
+    } else if (packed) {
         hipLaunchKernelGGL((project_write_packed_kernel<R, kFp8>), grid, dim3(256), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL((project_write_kernel<R, kFp8>), grid, dim3(256), 0, stream, a);
+    }
 }
 
 }  // namespace

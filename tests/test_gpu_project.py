@@ -95,7 +95,9 @@ def test_hidden_norm_in_place(oracle_lib):
 
 
 EXACT_SWEEP = [
-    # (N, hidden, L, nkv, R, bs, blocks, fp8, pad)
+    # (N, hidden, L, nkv, R, bs, blocks, fp8, pad); with a packed weight the
+    # column counts 2 L nkv 128 that are multiples of 512 run 128 x 512 tiles,
+    # the others (L nkv odd: the first three cases) 256 x 256 tiles
     (1, 64, 1, 1, 16, 1, 2, False, 0.0),
     (300, 256, 2, 2, 64, 16, 32, False, 0.1),
     (300, 512, 1, 3, 32, 4, 128, True, 0.2),
@@ -108,6 +110,11 @@ EXACT_SWEEP = [
     (333, 960, 1, 4, 16, 8, 64, True, 0.1),
     # the largest layer count: 32 layers x 2 kinds x 1 head = 64 heads
     (300, 128, 32, 1, 64, 16, 32, False, 0.1),
+    # 129 x 2 tiles of 128 x 512 with a packed weight: on a 256-CU device 256
+    # whole tiles and the last two tiles in 64-token halves in one launch,
+    # the very last half wholly past the last token
+    (16448, 128, 2, 2, 64, 16, 1100, False, 0.05),
+    (16448, 64, 1, 4, 32, 16, 1100, True, 0.05),
 ]
 
 
@@ -373,13 +380,17 @@ def _run_projection(wl, weight, R=None):
     return got
 
 
-@pytest.mark.parametrize("case", ["small-bf16", "small-fp8", "tail-bf16", "full-bf16", "full-fp8"])
+@pytest.mark.parametrize("case", ["small-bf16", "small-fp8", "tail-bf16", "halves-fp8", "full-bf16",
+                                  "full-fp8"])
 def test_packed_projection_equals_row_major(case):
-    """The packed kernel accumulates the same products in the same order as
-    the row-major one, so the caches it writes are identical byte for byte:
+    """The packed kernels accumulate the same products in the same order as
+    the row-major one, so the caches they write are identical byte for byte:
     on Gaussian data (no exact grid), with a ragged token tail and a k range
-    that ends inside a ring round, and at the full prefill size."""
-    if case == "small-bf16":
+    that ends inside a ring round, with whole tiles and 64-token halves in
+    one launch, and at the full prefill size."""
+    if case == "halves-fp8":
+        wl = W.project_custom(16400, 192, 1, 4, 64, 16, 1100, True, seed=34, pad_fraction=0.1)
+    elif case == "small-bf16":
         wl = W.project_custom(777, 448, 2, 2, 64, 16, 64, False, seed=31, pad_fraction=0.1)
     elif case == "small-fp8":
         wl = W.project_custom(513, 960, 3, 1, 32, 8, 256, True, seed=32, pad_fraction=0.2)
