@@ -578,8 +578,8 @@ __global__ __launch_bounds__(256, 1) void project_write_kernel(const ProjArgs a)
 // through LDS; the L2 serves it in 128-byte lines instead of 64-byte halves.
 // The token rows still go through LDS by DMA, in a ring of four stages; the
 // weight goes through a ring of four register stages (32 registers each).
-// Two arrangements of the four waves (WM x WN, each wave 128 tokens x 128
-// columns):
+// Two arrangements of the four waves (WM x WN, each wave 128 tokens, or 64
+// in the halves of the last round, x 128 columns):
 //   1 x 4: 128 tokens x 512 columns (four heads) per workgroup; the token
 //          rows (8 KB per stage) are shared by the four waves, and each wave
 //          loads its own head's weight, so no fragment is fetched twice: per
