@@ -86,7 +86,7 @@ int project_write(dspark_ctx_kv_writer *w, const void *states, int64_t num_ctx, 
     if (num_ctx == 0)
         return DSPARK_OK;
 
-    dspark::ProjArgs a{};
+    dspark::ProjArgs a;
     memset(&a, 0, sizeof a);
     a.z = static_cast<const uint16_t *>(states);
     a.W = static_cast<const uint16_t *>(kv_weight);
