@@ -115,6 +115,10 @@ EXACT_SWEEP = [
     # the very last half wholly past the last token
     (16448, 128, 2, 2, 64, 16, 1100, False, 0.05),
     (16448, 64, 1, 4, 32, 16, 1100, True, 0.05),
+    # one 128 x 512 tile in two halves: the second wholly past the only
+    # token, or holding one token
+    (1, 64, 2, 1, 16, 1, 2, True, 0.0),
+    (65, 128, 1, 2, 32, 4, 32, False, 0.0),
 ]
 
 
