@@ -102,8 +102,9 @@ constexpr uint32_t kSplitMaxWavesLayerSlotsFp8 = DSPARK_SPLIT_MAX_WAVES_LAYER_SL
 // long fp8 181.8 -> 176.7 us, per-layer slots fp8 -3.4%; bf16 -2.4% at 65536
 // waves and even at 32768; the general mapping 6% slower (bf16, nkv = 2,
 // 2048 waves) and even for fp8.  fp8 takes groups of two ({0,1}, {2,3},
-// {4}): with the XCD remap kept for large launches only, the fp8 prefill
-// 23.59 -> 23.12 us against groups of three, long fp8 even (177.0 vs 176.4).
+// {4}): measured while the XCD remap applied to large launches only, the fp8
+// prefill 23.59 -> 23.12 us against groups of three, long fp8 even (177.0 vs
+// 176.4).
 #ifndef DSPARK_GROUP_LAYERS_BF16
 #define DSPARK_GROUP_LAYERS_BF16 3
 #endif
@@ -132,18 +133,17 @@ constexpr int kGroupLayersGeneral = DSPARK_GROUP_LAYERS_GENERAL;
 constexpr bool kSlotFirst = DSPARK_SLOT_FIRST;
 constexpr int kRowsPerWave = 4;
 constexpr int kMaxChunk = 8;   // layers held in registers at once
-// Workgroup i runs on XCD i % 8; remapping gives each XCD a contiguous range
-// of rows.
-constexpr bool kXcdRemap = true;
-#ifndef DSPARK_REMAP_MIN_GROUPS
-#define DSPARK_REMAP_MIN_GROUPS 8192
+// Workgroup i runs on XCD i % 8; every launch remaps block ids so that each
+// XCD takes a contiguous range of rows.  The waves of one token's layers then
+// share one XCD's L2, which fetches the token's cos/sin row, slot and
+// position once instead of once per XCD (decode: 1.016x its algorithmic
+// bytes against 1.037x in round-robin order); long fp8 2.6% and the bf16
+// prefill 0.8% faster, the smaller launches even (decode -0.4%, TP-4 shard
+// -0.8%, fp8 prefill -0.3%, medians of 15 alternating rounds, twice).
+#ifndef DSPARK_XCD_REMAP
+#define DSPARK_XCD_REMAP 1
 #endif
-// Launches of fewer workgroups than this keep the hardware's round-robin
-// order over the XCDs.  Without the remap (medians of 7 alternating rounds):
-// fp8 prefill (4096 groups) -1.4%, decode (375) -3%, TP-4 shard -2.2%,
-// per-layer fp8 prefill -1.5%; bf16 prefill (10240) +0.8%, long fp8
-// (32768) +2.6%.
-constexpr uint32_t kRemapMinGroups = DSPARK_REMAP_MIN_GROUPS;
+constexpr bool kXcdRemap = DSPARK_XCD_REMAP;
 constexpr int kNumXcds = 8;
 
 // kChunk = layers held in registers per pass; kSinglePass: L == kChunk (the
@@ -189,17 +189,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
     uint32_t zero_after_args;
     {
         const uint32_t nu = a.num_units, sm = a.split_magic, tm = a.token_magic, gd = gridDim.x;
-        const int32_t xr = a.xcd_remap, nl = a.num_layers, bl = a.bs_log2;
+        const int32_t nl = a.num_layers, bl = a.bs_log2;
         const int64_t *ps = a.positions, *ss = a.slots;
         const void *kv = a.all_kv, *kw = a.k_norm_weight, *cs = a.cos_sin;
         asm("s_mov_b32 %0, 0"
             : "=s"(zero_after_args)
-            : "s"(nu), "s"(sm), "s"(tm), "s"(gd), "s"(xr), "s"(nl), "s"(nkv), "s"(bl), "s"(ps),
-              "s"(ss), "s"(kv), "s"(kw), "s"(cs));
+            : "s"(nu), "s"(sm), "s"(tm), "s"(gd), "s"(nl), "s"(nkv), "s"(bl), "s"(ps), "s"(ss),
+              "s"(kv), "s"(kw), "s"(cs));
     }
 
     uint32_t block = blockIdx.x + zero_after_args;
-    if (kXcdRemap && a.xcd_remap) {
+    if constexpr (kXcdRemap) {
         // blocks [0, full) are remapped so that XCD x owns one contiguous run
         const uint32_t full = gridDim.x - gridDim.x % kNumXcds;
         if (block < full) block = (block % kNumXcds) * (full / kNumXcds) + block / kNumXcds;
@@ -480,7 +480,6 @@ void launch_wpb(const CtxKvArgs &args, uint32_t waves, hipStream_t stream) {
     const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const dim3 block(64 * kWavesPerBlock);
     CtxKvArgs a = args;
-    a.xcd_remap = grid.x >= kRemapMinGroups;
     if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kChunk, kSinglePass, true, true, false,
                                                 kWavesPerBlock>), grid, block, 0, stream, a);
@@ -511,7 +510,6 @@ void launch_split(const CtxKvArgs &args, uint32_t waves, hipStream_t stream) {
     a.split_magic = div_magic(uint64_t{split} + 3, ng);
     const dim3 grid((split + 3) / 4);
     const dim3 block(256);
-    a.xcd_remap = grid.x >= kRemapMinGroups;
     if (a.layer_slots_on && a.nkv % kRowsPerWave == 0)
         hipLaunchKernelGGL((ctx_kv_write_kernel<R, kFp8, kGroup, true, true, true, true, 4>),
                            grid, block, 0, stream, a);
