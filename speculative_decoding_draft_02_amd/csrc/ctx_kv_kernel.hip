@@ -360,16 +360,25 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
         // one IEEE division gives every reciprocal of the chunk
         float my_scale = 1.0f, my_rcp = 1.0f;
         if constexpr (kFp8) {
-            int64_t soff = 0;
-            bool has = false;
+            // The chunk's scale offsets are wave-uniform: all of them are
+            // read as one batch of scalar loads, and the empty instruction
+            // below keeps the compiler from moving each load into a branch
+            // of its own lane's select (which waited once per offset: the
+            // fp8 prefill 2.6-5.4% slower, per-layer fp8 6%).
+            int64_t ko[kChunk], vo[kChunk];
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) {
-                if (lb + j < L) {
-                    if (lane == 2 * j) { soff = a.kscale_off[l0 + lb + j]; has = true; }
-                    if (lane == 2 * j + 1) { soff = a.vscale_off[l0 + lb + j]; has = true; }
-                }
+                const int l = l0 + (lb + j < L ? lb + j : L - 1);
+                ko[j] = a.kscale_off[l];
+                vo[j] = a.vscale_off[l];
             }
-            if (has) my_scale = a.scale0[soff];
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) asm("" : "+s"(ko[j]), "+s"(vo[j]));
+            int64_t soff = 0;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j)
+                soff = lane == 2 * j ? ko[j] : lane == 2 * j + 1 ? vo[j] : soff;
+            if (lane < 2 * (L - lb < kChunk ? L - lb : kChunk)) my_scale = a.scale0[soff];
             my_rcp = 1.0f / my_scale;
         }
 #pragma unroll
