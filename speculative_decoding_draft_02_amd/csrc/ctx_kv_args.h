@@ -31,7 +31,6 @@ struct CtxKvArgs {
     // wave, for wave -> token (d = nkv / 4); 0 = divide (see fast_div)
     uint32_t split_magic;
     uint32_t token_magic;
-    float zero;                  // 0.0f, read as a wave-uniform value
     int64_t cache_off[DSPARK_MAX_LAYERS];  // elements from cache0
     int64_t kscale_off[DSPARK_MAX_LAYERS]; // floats from scale0
     int64_t vscale_off[DSPARK_MAX_LAYERS]; // floats from scale0

@@ -120,9 +120,6 @@ constexpr int kGroupLayersGeneral = DSPARK_GROUP_LAYERS_GENERAL;
 #ifndef DSPARK_FASTDIV
 #define DSPARK_FASTDIV 1
 #endif
-#ifndef DSPARK_DOT2_SZERO
-#define DSPARK_DOT2_SZERO 0
-#endif
 #ifndef DSPARK_SLOT_FIRST
 #define DSPARK_SLOT_FIRST 1
 #endif
@@ -386,8 +383,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void ctx_kv_write_kernel(const
             const int l = lb + j;
             if (l >= L) break;
             uint32_t kb[4];
-            norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb,
-                         DSPARK_DOT2_SZERO ? a.zero : 0.0f);
+            norm_rope<R>(dk[j], wv[j], a.eps, c, cs, kb);
             // element index of this lane's row start (chunk excluded) in layer l
             int64_t rbase = a.cache_off[l0 + l] + row - c * 8;
             bool store = true;
@@ -548,12 +544,19 @@ void launch_one(const CtxKvArgs &args, hipStream_t stream) {
         launch_split<R, kFp8, 1>(a, waves, stream);
         return;
     }
+    // a split launch numbers its waves in 32 bits (wave count times layer
+    // groups); a write too large for that keeps whole row groups per wave
+    auto split_fits = [&](int group) {
+        const uint64_t ng = (static_cast<uint64_t>(a.num_layers) + group - 1) / group;
+        return uint64_t{waves} * ng + 4 < (uint64_t{1} << 32);
+    };
     constexpr int kGroup = kFp8 ? kGroupLayersFp8 : kGroupLayersBf16;
-    if (kGroup > 1 && !general && a.num_layers > kGroup) {
+    if (kGroup > 1 && !general && a.num_layers > kGroup && split_fits(kGroup)) {
         launch_split<R, kFp8, kGroup>(a, waves, stream);
         return;
     }
-    if (kGroupLayersGeneral > 1 && general && a.num_layers > kGroupLayersGeneral) {
+    if (kGroupLayersGeneral > 1 && general && a.num_layers > kGroupLayersGeneral &&
+        split_fits(kGroupLayersGeneral)) {
         launch_split<R, kFp8, kGroupLayersGeneral>(a, waves, stream);
         return;
     }

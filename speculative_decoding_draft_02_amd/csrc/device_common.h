@@ -189,8 +189,7 @@ __device__ __forceinline__ uint2 pack_fp8(const uint32_t (&b)[4], float s, float
 // half of the rotated dims), or (1, 0) on lanes past the rotated dims.
 template <int R>
 __device__ __forceinline__ void norm_rope(const uint4 &d, const uint4 &w, float eps, int c,
-                                          const uint32_t (&cs)[8], uint32_t (&out)[4],
-                                          float zero = 0.0f) {
+                                          const uint32_t (&cs)[8], uint32_t (&out)[4]) {
     constexpr int kRotLanes = R / 8;   // lanes holding rotated dims
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -214,8 +213,8 @@ __device__ __forceinline__ void norm_rope(const uint4 &d, const uint4 &w, float 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t pb = rope_partner<R>(yb[k], c);
-        const float r0 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x05040100u), cs[2 * k], zero);
-        const float r1 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x07060302u), cs[2 * k + 1], zero);
+        const float r0 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x05040100u), cs[2 * k], 0.0f);
+        const float r1 = dot2_bf16(__builtin_amdgcn_perm(pb, yb[k], 0x07060302u), cs[2 * k + 1], 0.0f);
         out[k] = (c < kRotLanes) ? pack_bf16(r0, r1) : yb[k];
     }
 }
